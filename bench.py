@@ -1,0 +1,251 @@
+"""Benchmark: ring AllReduce over R virtual ranks on one MI355X.
+
+Default workload: R=8 virtual ranks, fp32, 64 MiB per rank, SUM, 4 slices.  One
+step is one in-place AllReduce call (2(R-1) ring hops) over all R rank buffers,
+inputs resident in HBM.
+
+value = algorithmic HBM bytes per call / time per call, with the algorithmic
+bytes of the in-place ring: each ReduceScatter hop reads the incoming and local
+chunk and writes the folded one (3 chunk transfers), each AllGather hop reads and
+writes one chunk (2), so B = 5 (R-1) N for N bytes per rank.
+
+Prints one JSON line (rank 0).  Also reports:
+  roofline      -- the ring kernel against MI355X's 8 TB/s HBM peak: its average
+                   launch duration from HIP events on the launch stream around the
+                   timed region; `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+                   record in profiles/ when it was taken on this kernel source;
+  cpu_baseline  -- the single-threaded CPU oracle on the same inputs (test
+                   infrastructure; timed only, never on the product path), which
+                   also cross-checks one GPU call;
+  copy_ceiling  -- the library's streaming copy kernel over 1 GiB + 1 GiB.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) for ring AllReduce over R virtual ranks"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="r8_fp32_64MiB",
+                    help="r8_fp32_64MiB | r8_bf16_256MiB | r64_fp32_32MiB | worked_example | "
+                         "r16_sweep:K[:op[:nslices]]")
+    ap.add_argument("--sync", default=None, help="auto | p2p | barrier | launch")
+    ap.add_argument("--team", type=int, default=0)
+    ap.add_argument("--block", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    return ap.parse_args()
+
+
+def pick_workload(name):
+    import workloads
+    if name.startswith("r16_sweep:"):
+        parts = name.split(":")
+        k = int(parts[1])
+        op = parts[2] if len(parts) > 2 else "sum"
+        ns = int(parts[3]) if len(parts) > 3 else 4
+        return workloads.r16_sweep(k, op, ns)
+    return workloads.ALL[name]
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ring_allreduce_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_name, digest):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for this
+    kernel source (profiles/traffic_<workload>.json), or None if stale/absent."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != digest:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the virtual ranks of the ring all live in one "
+              "MI355X's HBM, and this build runs nothing across GPUs. Use --gpus 1.",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ring_allreduce_amd as rr
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = pick_workload(args.workload)
+    if args.sync:
+        w = w.with_(sync=args.sync)
+    opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags)
+    rr.init()
+    p = rr.plan(w.R, w.count, w.dtype, w.nslices, **opts)
+    log(f"workload {w.name}: R={w.R} {w.dtype} {w.op} {w.bytes_per_rank / 2**20:.1f} MiB/rank "
+        f"nslices={w.nslices} plan={p}")
+
+    t = time.time()
+    x = workloads.inputs(w)
+    log(f"inputs generated in {time.time() - t:.1f} s")
+    torch_dt = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    raw_t = torch.int16 if w.dtype == "bf16" else torch.int32
+    raw_np = np.int16 if w.dtype == "bf16" else np.int32
+    slabs = rr.make_slabs(w.R, w.count, torch_dt, device="cuda")
+    for r in range(w.R):
+        slabs.ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
+    pristine = slabs.storage.clone()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rr.allreduce_ring(slabs.ranks, w.op, w.nslices, **opts)
+
+    # one checked call on the pristine inputs, kept for the CPU cross-check
+    step()
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    first_result = [slabs.ranks[r].view(raw_t).cpu().numpy() for r in range(w.R)]
+
+    for _ in range(args.warmup):
+        step()
+    slabs.storage.copy_(pristine)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+
+    # timed region: exactly K steps
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    rr.check_kernel_error()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    B = p["hbm_bytes"]
+    value = B / (ms_per_step * 1e-3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}) "
+        f"-> {value:.1f} GB/s algorithmic")
+
+    # The ring kernel's average launch duration: HIP events on the launch stream
+    # around the timed region, divided by the launches it holds (back to back).
+    per_call = p["launches"]
+    avg_launch_ms = ev0.elapsed_time(ev1) / (args.steps * per_call)
+    bytes_per_launch = B / per_call
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = stored_traffic(w.name, digest)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "ring_kernel", "launch_ms_avg": round(avg_launch_ms, 5),
+                "launches_timed": args.steps * per_call, "bytes_per_launch": int(bytes_per_launch),
+                "kernel_source_digest": digest}
+
+    copy_ceiling = None
+    if not args.no_copy_ceiling:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            rr.hbm_copy(dst, src)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        reps = 10
+        for _ in range(reps):
+            rr.hbm_copy(dst, src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        copy_ceiling = {"bytes": 2 * n, "ms": round(ms, 4),
+                        "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+        log(f"copy ceiling: {copy_ceiling}")
+
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        import oracle  # test infrastructure: the CPU baseline leg only
+        runs, spent = 0, 0.0
+        expect = None
+        while runs == 0 or (spent < args.cpu_seconds and runs < 20):
+            bufs = [a.copy() for a in x]
+            t = time.perf_counter()
+            oracle.allreduce(bufs, w.op)
+            spent += time.perf_counter() - t
+            runs += 1
+            expect = bufs
+        per = spent / runs
+        ok = all(np.array_equal(first_result[r].view(np.uint8), expect[r].view(np.uint8))
+                 for r in range(w.R))
+        cpu_baseline = {"value": round(B / per / 1e9, 3), "unit": "GB/s", "cores": 1,
+                        "kind": "oracle", "ms_per_call": round(per * 1e3, 1),
+                        "sample": f"the full {w.name} input, {runs} call(s) of the single-threaded "
+                                  f"C oracle ({spent:.1f} s)",
+                        "gpu_matches_oracle_bitwise": bool(ok),
+                        "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+        log(f"cpu baseline: {cpu_baseline}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic", "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": w.name, "R": w.R, "bytes_per_rank": w.bytes_per_rank,
+                   "op": w.op, "nslices": w.nslices, "sync": p["sync"], "team": p["team"],
+                   "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
+                   "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
+        "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    sys.exit(main())

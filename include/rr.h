@@ -1,0 +1,278 @@
+/*
+ * rr.h -- ring AllReduce over virtual ranks on one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of librr.so.  Plain pointers and sizes only.
+ *
+ * THE OPERATION.  The post "Why AllReduce = ReduceScatter + AllGather -- with
+ * NCCL Ring AllReduce" (loosp.cn) defines it:
+ *   section 1  -- R ranks each hold a buffer cut into R chunks; afterwards every
+ *                 rank holds S_k, the reduction over all ranks of chunk k, for
+ *                 every k;
+ *   section 4  -- the ranks form the ring 0 -> 1 -> ... -> R-1 -> 0;
+ *   section 5  -- ReduceScatter: R-1 rounds; in round s rank r sends chunk
+ *                 (r - s + 1) mod R to rank r + 1, which folds it into its own
+ *                 copy (incoming first); afterwards rank r owns chunk (r+1) mod R;
+ *   section 6  -- AllGather: R-1 rounds of receive + copy + send, no arithmetic;
+ *                 in round t rank r forwards chunk (r + 2 - t) mod R;
+ *   section 12 -- the data are cut into R contiguous pieces.
+ * Here the R ranks are virtual: rank r is the device buffer bufs[r], and a
+ * "send" from rank r is a store into bufs[(r + 1) mod R].  Every hop therefore
+ * moves exactly the chunk traffic of the real ring: a ReduceScatter hop reads
+ * the incoming chunk and the local chunk and writes the folded chunk; an
+ * AllGather hop reads and writes one chunk.
+ *
+ * CHUNKS.  chunk_len = ceil(count / R) rounded up to a whole 16-byte vector
+ * (4 int32/fp32 or 8 bf16 elements); chunk c covers elements
+ * [c*chunk_len, min((c+1)*chunk_len, count)) and may be empty.  Each chunk is
+ * further cut into `nslices` slices of equal nominal length (vector aligned);
+ * slices only schedule work: results do not depend on nslices.
+ *
+ * ARITHMETIC, one fold per ReduceScatter hop, local = incoming (op) local:
+ *   int32 SUM  wraps modulo 2^32          int32 MAX  signed comparison
+ *   fp32  SUM  one binary32 addition,     fp32  MAX  the local value if it
+ *              round to nearest even                 compares greater, else
+ *   bf16  SUM  the exact sum rounded to              the incoming value
+ *              bf16, nearest even; a NaN  bf16  MAX  as fp32 MAX, keeping the
+ *              result is 0x7FC0                      winner's bits
+ * So the element result of chunk c is the left fold over ranks c, c+1, ...,
+ * c+R-1 (mod R), rounded to the storage type after every step.
+ *
+ * HAND-OFF.  One persistent kernel runs every hop.  Each slice is split among a
+ * team of workgroups; a (slice, team member) pair is a lane, and workgroups own
+ * (virtual rank, lane) pairs.  Every lane is an independent context with one
+ * 64-bit signal per rank, so lanes pipeline against each other.  After a hop a
+ * producer adds 1 to its consumer's signal (the counting barrier of the DeepEP
+ * pull request "make the rail barrier a counting barrier", section "Fix"); the
+ * consumer advances a private shadow by the number of arrivals it expects and
+ * waits until the signal reaches the shadow, with the rolling comparison the
+ * NCCL GIN documentation describes (2kiu.com article on NCCL GIN, section
+ * "Signals and counters"), so counters never need a reset.  A signal never has
+ * two producers of the same rank: an anonymous count could then be met by one
+ * producer running a hop ahead while another still writes (the same pull
+ * request, section "Scoped to the rail team").
+ *
+ * STREAMS AND ORDER.  Every entry point that takes a stream enqueues work on it
+ * and returns once the work is enqueued (the status covers validation and
+ * enqueue only).  Device-side failures (a wait that timed out) surface through
+ * rr_last_kernel_error after the stream has drained.  Calls on one device share
+ * one signal workspace, so they must not overlap in time: issue them on one
+ * stream, or order them yourself.
+ *
+ * OWNERSHIP.  The caller owns every buffer and stream; the library never keeps
+ * a buffer pointer beyond the call.  The library owns one small per-device
+ * workspace (signals, shadows, the error record), allocated on the first call
+ * on a device (or by rr_init) and freed by rr_finalize.  The first call on a
+ * device must therefore not happen under stream capture.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RR_ABI_VERSION 1
+#define RR_MAX_RANKS 64      /* virtual ranks per call */
+#define RR_MAX_SLICES 1024   /* slices per call; slices * team * R <= 65536 */
+
+typedef enum { RR_INT32 = 0, RR_FP32 = 1, RR_BF16 = 2 } rr_dtype_t;
+
+typedef enum { RR_SUM = 0, RR_MAX = 1 } rr_op_t;
+
+typedef enum {
+    RR_OK = 0,
+    RR_ERR_INVALID = 1,     /* bad argument; nothing was enqueued */
+    RR_ERR_UNSUPPORTED = 2, /* valid, but the requested mode cannot run it */
+    RR_ERR_HIP = 3,         /* a HIP runtime call failed */
+    RR_ERR_TIMEOUT = 4,     /* a device wait gave up (see rr_error_record_t) */
+    RR_ERR_NOMEM = 5        /* device or host allocation failed */
+} rr_status_t;
+
+/* How consecutive hops hand off. */
+typedef enum {
+    RR_SYNC_AUTO = 0,    /* P2P when every workgroup can be resident, else LAUNCH */
+    RR_SYNC_P2P = 1,     /* persistent kernel; a consumer waits for its predecessor
+                            rank's workgroup in the same lane only (1 arrival per hop) */
+    RR_SYNC_BARRIER = 2, /* persistent kernel; every hop ends with a counting barrier
+                            over all R ranks of the lane: each workgroup adds 1 to
+                            every other rank's signal, a waiter expects R-1 */
+    RR_SYNC_LAUNCH = 3   /* one kernel launch per hop; stream order is the barrier */
+} rr_sync_t;
+
+/* Fault injection, for failure tests only.  Each makes one waiter's wait
+   unsatisfiable, so that it times out and every workgroup still exits. */
+#define RR_INJECT_EXTRA_EXPECTED 0x1u /* rank 0, context 0 expects one arrival too many
+                                         at its first wait */
+#define RR_INJECT_DROP_ARRIVAL   0x2u /* rank 0, context 0 skips its first arrival */
+
+/* Flags. */
+#define RR_FLAG_NO_XCD_MAP       0x1u /* plain block -> (rank, slice) order */
+#define RR_FLAG_NO_POINTER_CHECK 0x2u /* skip the per-call allocation-extent check */
+#define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
+                                         hipLaunchCooperativeKernel (co-residency
+                                         guaranteed by the runtime; otherwise the
+                                         library checks grid <= resident capacity and
+                                         the bounded waits catch a starved grid) */
+
+typedef struct {
+    int32_t sync;        /* rr_sync_t */
+    int32_t team;        /* workgroups per (rank, slice); 0 = choose */
+    int32_t block;       /* threads per workgroup: 0 (= 512), 256, 512 or 1024 */
+    int32_t reserved;
+    uint64_t timeout_ns; /* bound on every device wait; 0 = 2 s */
+    uint32_t inject;     /* RR_INJECT_* */
+    uint32_t flags;      /* RR_FLAG_* */
+} rr_options_t;
+
+/* What a call will run (rr_plan_query). */
+typedef struct {
+    int32_t sync;        /* rr_sync_t actually used (never AUTO) */
+    int32_t team;
+    int32_t block;
+    int32_t grid;        /* workgroups per launch */
+    int32_t launches;    /* kernel launches per call */
+    int32_t xcd_map;     /* 1 if a slice's ranks share one XCD */
+    int32_t cooperative; /* 1 if launched with hipLaunchCooperativeKernel */
+    int32_t resident_max;/* workgroups the device can hold at once for this kernel */
+    uint64_t chunk_len;  /* elements */
+    uint64_t slice_len;  /* elements */
+    uint64_t sub_len;    /* elements per team member */
+    uint64_t hbm_bytes;  /* algorithmic bytes read + written by one call */
+} rr_plan_t;
+
+/* Device-side failure record (rr_last_kernel_error).  Following the DeepEP
+   pull request (section "Fix"), a counting signal cannot name the missing peer,
+   so the record gives the signal and how many arrivals were missing. */
+typedef struct {
+    int32_t status;    /* RR_OK or RR_ERR_TIMEOUT */
+    int32_t ctx;       /* context (lane = slice * team + member) of the waiter */
+    int32_t waiter;    /* its virtual rank */
+    int32_t hop;       /* hop (or barrier step) it was about to start */
+    uint64_t expected; /* signal value it waited for */
+    uint64_t observed; /* last value it read; expected - observed are missing */
+} rr_error_record_t;
+
+typedef void *rr_stream_t; /* a hipStream_t; NULL is the null stream */
+
+/* ------------------------------------------------------------ collectives */
+
+/* AllReduce (sections 1 and 4-6 of the loosp.cn post).  In place: bufs is a host
+   array of R device pointers, each to `count` elements of `dt`, 16-byte aligned,
+   pairwise disjoint, on the current device.  Afterwards every bufs[r] holds the
+   reduction described above.  R == 1 or count == 0 is a no-op.
+   Errors: RR_ERR_INVALID (R outside 1..64, nslices outside 1..1024, NULL or
+   misaligned or overlapping buffers, a buffer not inside one device allocation,
+   unknown dtype or op), RR_ERR_UNSUPPORTED (a persistent mode was requested but
+   the grid cannot be resident), RR_ERR_HIP, RR_ERR_NOMEM. */
+rr_status_t allreduce_ring(void *const *bufs, int R, size_t count, rr_dtype_t dt, rr_op_t op,
+                           int nslices, rr_stream_t stream);
+
+/* ReduceScatter (section 5).  In place, arguments as allreduce_ring.  Afterwards
+   chunk (r + 1) mod R of bufs[r] holds the finished reduction of that chunk, and
+   chunk c of bufs[r] holds the ring's partial fold of ranks c, c+1, ..., r (for
+   c == r: rank r's own input, untouched). */
+rr_status_t reduce_scatter_ring(void *const *bufs, int R, size_t count, rr_dtype_t dt,
+                                rr_op_t op, int nslices, rr_stream_t stream);
+
+/* AllGather (section 6).  In place, arguments as allreduce_ring without an op.
+   Before: chunk (r + 1) mod R of bufs[r] holds the data to spread.  Afterwards
+   chunk c of every buffer is a bitwise copy of chunk c of bufs[(c - 1) mod R]. */
+rr_status_t all_gather_ring(void *const *bufs, int R, size_t count, rr_dtype_t dt, int nslices,
+                            rr_stream_t stream);
+
+/* The same three with explicit options (opt may be NULL for the defaults). */
+rr_status_t allreduce_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_t dt, rr_op_t op,
+                              int nslices, const rr_options_t *opt, rr_stream_t stream);
+rr_status_t reduce_scatter_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_t dt,
+                                   rr_op_t op, int nslices, const rr_options_t *opt,
+                                   rr_stream_t stream);
+rr_status_t all_gather_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_t dt,
+                               int nslices, const rr_options_t *opt, rr_stream_t stream);
+
+/* The plan a call with these arguments would run; no device work.  `phase` is
+   0 for AllReduce, 1 for ReduceScatter, 2 for AllGather.  Errors as the call. */
+rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int phase,
+                          const rr_options_t *opt, rr_plan_t *out);
+
+/* ------------------------------------------------------- counting barrier */
+
+/* A standalone set of counting signals: `ncontexts` contexts of `nwaiters`
+   waiters, one 64-bit signal and one shadow each (DeepEP pull request, section
+   "Fix": one signal per waiter whatever the team size).  Caller-owned; lives in
+   device memory of the current device. */
+typedef struct rr_counting_barrier rr_counting_barrier_t;
+
+/* Errors: RR_ERR_INVALID (nwaiters outside 1..64, ncontexts outside 1..1024,
+   out NULL), RR_ERR_NOMEM, RR_ERR_HIP. */
+rr_status_t counting_barrier_create(int nwaiters, int ncontexts, rr_counting_barrier_t **out);
+
+/* Frees the object; waits for its device work first.  NULL is a no-op. */
+rr_status_t counting_barrier_destroy(rr_counting_barrier_t *b);
+
+/* Zeroes every signal and shadow, ordered on `stream`.  Only while no kernel
+   uses the barrier: a reset must not race other updates (2kiu.com article on
+   NCCL GIN, section "Signal methods"). */
+rr_status_t counting_barrier_reset(rr_counting_barrier_t *b, rr_stream_t stream);
+
+/* Presets every signal and shadow to `value` (wrap tests); quiescent only. */
+rr_status_t counting_barrier_preset(rr_counting_barrier_t *b, uint64_t value, rr_stream_t stream);
+
+/* Reads one waiter's signal and shadow, synchronously (waits for the device). */
+rr_status_t counting_barrier_read(rr_counting_barrier_t *b, int ctx, int waiter, uint64_t *value,
+                                  uint64_t *shadow);
+
+/* Runs `nsteps` barrier steps over the first `ncontexts` contexts with R
+   waiters each, one workgroup per (context, waiter), in one kernel.  Per step a
+   waiter arrives (opt->sync RR_SYNC_BARRIER or AUTO: adds 1 to every other
+   waiter's signal in its context; RR_SYNC_P2P: adds 1 to its successor's) and
+   then advances its shadow by `expected_per_step` and waits for its own signal.
+   The right expectation is R-1 (barrier) or 1 (p2p); a larger one times out
+   (RR_ERR_TIMEOUT from rr_last_kernel_error, with the missing count).  With
+   nsteps == 0 it launches the same kernel doing nothing, to time the launch.
+   Errors: RR_ERR_INVALID (R > nwaiters, ncontexts > the object's, nsteps < 0),
+   RR_ERR_UNSUPPORTED (grid cannot be resident), RR_ERR_HIP. */
+rr_status_t counting_barrier_run(rr_counting_barrier_t *b, int R, int nsteps, int ncontexts,
+                                 uint64_t expected_per_step, const rr_options_t *opt,
+                                 rr_stream_t stream);
+
+/* ---------------------------------------------------------------- support */
+
+/* Waits for `stream`, then reports and clears the device's failure record.
+   Returns RR_OK if no wait failed since the last call, else the recorded status
+   (RR_ERR_TIMEOUT) with the record in *rec (rec may be NULL).  While a failure
+   is recorded every ring and barrier kernel on the device returns at once
+   without touching data (sticky), so check after a call whose results matter.
+   Clearing also resets the ring workspace's signals and shadows. */
+rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t *rec);
+
+/* Creates the current device's workspace now (so that later calls allocate
+   nothing).  Errors: RR_ERR_HIP, RR_ERR_NOMEM. */
+rr_status_t rr_init(void);
+
+/* Presets every ring-workspace signal and shadow of the current device to
+   `value`, ordered on `stream` (tests of the rolling comparison near 2^64). */
+rr_status_t rr_workspace_preset(uint64_t value, rr_stream_t stream);
+
+/* Copies `bytes` bytes from src to dst (device pointers, 16-byte aligned, not
+   overlapping) with the library's streaming copy kernel: the bandwidth
+   reference and counter calibration for the ring kernels.  Errors:
+   RR_ERR_INVALID, RR_ERR_HIP. */
+rr_status_t rr_hbm_copy(void *dst, const void *src, size_t bytes, rr_stream_t stream);
+
+/* Human-readable name of a status. */
+const char *rr_status_string(rr_status_t s);
+
+/* RR_ABI_VERSION of the loaded library. */
+int rr_abi_version(void);
+
+/* Frees every device's workspace.  No call may be in flight. */
+void rr_finalize(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,340 @@
+"""Ring AllReduce over virtual ranks on one MI355X -- Python binding.
+
+A thin ctypes layer over ``librr.so`` (declared in ``include/rr.h``).  It only
+marshals arguments: tensors become device pointers, dtype and op names become
+enum values, a torch stream becomes a ``hipStream_t``.  Every step of the
+collective runs in the library's HIP kernels; there is no fallback.  Importing
+this package without a built ``librr.so`` raises.
+
+PyTorch supplies device memory and streams.  ``import torch`` happens first so
+that ``librr.so`` binds to the same HIP runtime instance as torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # noqa: F401  (loads the HIP runtime librr.so must share)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python ring_allreduce_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+RR_MAX_RANKS = 64
+RR_MAX_SLICES = 1024
+
+DTYPES = {"int32": 0, "fp32": 1, "bf16": 2}
+OPS = {"sum": 0, "max": 1}
+SYNCS = {"auto": 0, "p2p": 1, "barrier": 2, "launch": 3}
+SYNC_NAMES = {v: k for k, v in SYNCS.items()}
+PHASES = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+
+STATUS = {0: "RR_OK", 1: "RR_ERR_INVALID", 2: "RR_ERR_UNSUPPORTED", 3: "RR_ERR_HIP",
+          4: "RR_ERR_TIMEOUT", 5: "RR_ERR_NOMEM"}
+RR_OK, RR_ERR_INVALID, RR_ERR_UNSUPPORTED, RR_ERR_HIP, RR_ERR_TIMEOUT, RR_ERR_NOMEM = range(6)
+
+INJECT_EXTRA_EXPECTED = 0x1
+INJECT_DROP_ARRIVAL = 0x2
+FLAG_NO_XCD_MAP = 0x1
+FLAG_NO_POINTER_CHECK = 0x2
+FLAG_COOPERATIVE = 0x4
+
+_TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16"}
+ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("sync", ctypes.c_int32), ("team", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
+                ("inject", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("sync", ctypes.c_int32), ("team", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("xcd_map", ctypes.c_int32), ("cooperative", ctypes.c_int32),
+                ("resident_max", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
+                ("slice_len", ctypes.c_uint64), ("sub_len", ctypes.c_uint64),
+                ("hbm_bytes", ctypes.c_uint64)]
+
+
+class ErrorRecord(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("ctx", ctypes.c_int32), ("waiter", ctypes.c_int32),
+                ("hop", ctypes.c_int32), ("expected", ctypes.c_uint64),
+                ("observed", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_u64 = ctypes.c_uint64
+_OPT = ctypes.POINTER(Options)
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_allreduce_ring_ex = _sig("allreduce_ring_ex", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _OPT, _vp)
+_reduce_scatter_ring_ex = _sig("reduce_scatter_ring_ex", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i,
+                               _i, _OPT, _vp)
+_all_gather_ring_ex = _sig("all_gather_ring_ex", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _OPT, _vp)
+_allreduce_ring = _sig("allreduce_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _vp)
+_reduce_scatter_ring = _sig("reduce_scatter_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _vp)
+_all_gather_ring = _sig("all_gather_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _vp)
+_plan_query = _sig("rr_plan_query", _i, _i, _sz, _i, _i, _i, _OPT, ctypes.POINTER(_Plan))
+_cb_create = _sig("counting_barrier_create", _i, _i, _i, ctypes.POINTER(_vp))
+_cb_destroy = _sig("counting_barrier_destroy", _i, _vp)
+_cb_reset = _sig("counting_barrier_reset", _i, _vp, _vp)
+_cb_preset = _sig("counting_barrier_preset", _i, _vp, _u64, _vp)
+_cb_read = _sig("counting_barrier_read", _i, _vp, _i, _i, ctypes.POINTER(_u64), ctypes.POINTER(_u64))
+_cb_run = _sig("counting_barrier_run", _i, _vp, _i, _i, _i, _u64, _OPT, _vp)
+_last_kernel_error = _sig("rr_last_kernel_error", _i, _vp, ctypes.POINTER(ErrorRecord))
+_init = _sig("rr_init", _i)
+_workspace_preset = _sig("rr_workspace_preset", _i, _u64, _vp)
+_hbm_copy = _sig("rr_hbm_copy", _i, _vp, _vp, _sz, _vp)
+_status_string = _sig("rr_status_string", ctypes.c_char_p, _i)
+_abi_version = _sig("rr_abi_version", _i)
+_finalize = _sig("rr_finalize", None)
+
+# Every symbol include/rr.h declares, for the export check.
+EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
+            "reduce_scatter_ring_ex", "all_gather_ring_ex", "rr_plan_query",
+            "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
+            "counting_barrier_preset", "counting_barrier_read", "counting_barrier_run",
+            "rr_last_kernel_error", "rr_init", "rr_workspace_preset", "rr_hbm_copy",
+            "rr_status_string", "rr_abi_version", "rr_finalize"]
+
+
+class RRError(RuntimeError):
+    def __init__(self, status: int, what: str, record: dict | None = None):
+        self.status = status
+        self.record = record
+        msg = f"{what}: {status_string(status)}"
+        if record:
+            missing = record["expected"] - record["observed"]
+            msg += (f" (context {record['ctx']}, waiter rank {record['waiter']}, hop {record['hop']}: "
+                    f"expected signal {record['expected']}, saw {record['observed']}, "
+                    f"{missing} arrival(s) missing)")
+        super().__init__(msg)
+
+
+def status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def abi_version() -> int:
+    return _abi_version()
+
+
+def _check(status: int, what: str) -> None:
+    if status != RR_OK:
+        raise RRError(status, what)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _options(sync="auto", team=0, block=0, timeout_ns=0, inject=0, flags=0):
+    return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, 0,
+                   timeout_ns, inject, flags)
+
+
+def _buffers(tensors):
+    if not tensors:
+        raise ValueError("need at least one rank buffer")
+    t0 = tensors[0]
+    if t0.dtype not in _TORCH_DTYPES:
+        raise TypeError(f"unsupported dtype {t0.dtype}; use int32, float32 or bfloat16")
+    for t in tensors:
+        if t.device.type != "cuda" or t.device != t0.device:
+            raise ValueError("all rank buffers must be on the same GPU")
+        if t.dtype != t0.dtype or t.numel() != t0.numel():
+            raise ValueError("rank buffers must share dtype and length")
+        if not t.is_contiguous():
+            raise ValueError("rank buffers must be contiguous")
+    ptrs = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return ptrs, t0.numel(), _TORCH_DTYPES[t0.dtype]
+
+
+def allreduce_ring(tensors, op: str = "sum", nslices: int = 1, *, stream=None, **opts) -> None:
+    """In-place ring AllReduce over the list of R rank buffers (one per virtual rank)."""
+    ptrs, count, dt = _buffers(tensors)
+    with torch.cuda.device(tensors[0].device):
+        s = _stream_handle(stream)
+        if opts:
+            o = _options(**opts)
+            st = _allreduce_ring_ex(ptrs, len(tensors), count, DTYPES[dt], OPS[op], nslices,
+                                    ctypes.byref(o), s)
+        else:
+            st = _allreduce_ring(ptrs, len(tensors), count, DTYPES[dt], OPS[op], nslices, s)
+    _check(st, "allreduce_ring")
+
+
+def reduce_scatter_ring(tensors, op: str = "sum", nslices: int = 1, *, stream=None, **opts) -> None:
+    """In-place ring ReduceScatter: afterwards rank r owns chunk (r + 1) mod R."""
+    ptrs, count, dt = _buffers(tensors)
+    with torch.cuda.device(tensors[0].device):
+        s = _stream_handle(stream)
+        if opts:
+            o = _options(**opts)
+            st = _reduce_scatter_ring_ex(ptrs, len(tensors), count, DTYPES[dt], OPS[op], nslices,
+                                         ctypes.byref(o), s)
+        else:
+            st = _reduce_scatter_ring(ptrs, len(tensors), count, DTYPES[dt], OPS[op], nslices, s)
+    _check(st, "reduce_scatter_ring")
+
+
+def all_gather_ring(tensors, nslices: int = 1, *, stream=None, **opts) -> None:
+    """In-place ring AllGather of chunk (r + 1) mod R of every rank r."""
+    ptrs, count, dt = _buffers(tensors)
+    with torch.cuda.device(tensors[0].device):
+        s = _stream_handle(stream)
+        if opts:
+            o = _options(**opts)
+            st = _all_gather_ring_ex(ptrs, len(tensors), count, DTYPES[dt], nslices,
+                                     ctypes.byref(o), s)
+        else:
+            st = _all_gather_ring(ptrs, len(tensors), count, DTYPES[dt], nslices, s)
+    _check(st, "all_gather_ring")
+
+
+def allreduce_ring_ptrs(ptrs, count: int, dtype: str, op: str = "sum", nslices: int = 1,
+                        stream=0, phase: str = "allreduce", **opts) -> int:
+    """Raw-pointer call; returns the status instead of raising (argument tests)."""
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs) if ptrs is not None else None
+    o = _options(**opts)
+    R = len(ptrs) if ptrs is not None else 0
+    if phase == "allreduce":
+        return _allreduce_ring_ex(arr, R, count, DTYPES.get(dtype, dtype if isinstance(dtype, int) else 99),
+                                  OPS.get(op, op if isinstance(op, int) else 99), nslices,
+                                  ctypes.byref(o), stream)
+    if phase == "reduce_scatter":
+        return _reduce_scatter_ring_ex(arr, R, count, DTYPES[dtype], OPS[op], nslices,
+                                       ctypes.byref(o), stream)
+    return _all_gather_ring_ex(arr, R, count, DTYPES[dtype], nslices, ctypes.byref(o), stream)
+
+
+def plan(R: int, count: int, dtype: str, nslices: int = 1, phase: str = "allreduce", **opts) -> dict:
+    """The launch plan a call with these arguments would run (needs a GPU)."""
+    p = _Plan()
+    o = _options(**opts)
+    _check(_plan_query(R, count, DTYPES[dtype], nslices, PHASES[phase], ctypes.byref(o),
+                       ctypes.byref(p)), "rr_plan_query")
+    d = {f: getattr(p, f) for f, _ in p._fields_}
+    d["sync"] = SYNC_NAMES[d["sync"]]
+    return d
+
+
+def last_kernel_error(stream=None):
+    """(status, record dict or None) of the device's failure record; clears it."""
+    rec = ErrorRecord()
+    st = _last_kernel_error(_stream_handle(stream), ctypes.byref(rec))
+    return st, (rec.as_dict() if st == RR_ERR_TIMEOUT else None)
+
+
+def check_kernel_error(stream=None) -> None:
+    """Raise RRError if any device wait failed since the last check."""
+    st, rec = last_kernel_error(stream)
+    if st != RR_OK:
+        raise RRError(st, "device wait", rec)
+
+
+def init() -> None:
+    _check(_init(), "rr_init")
+
+
+def finalize() -> None:
+    _finalize()
+
+
+def workspace_preset(value: int, stream=None) -> None:
+    _check(_workspace_preset(value, _stream_handle(stream)), "rr_workspace_preset")
+
+
+def hbm_copy(dst, src, stream=None) -> None:
+    """dst <- src with the library's streaming copy kernel (byte copy of src)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("destination too small")
+    _check(_hbm_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream_handle(stream)), "rr_hbm_copy")
+
+
+class CountingBarrier:
+    """A set of counting signals: ``ncontexts`` x ``nwaiters``, 64-bit each."""
+
+    def __init__(self, nwaiters: int, ncontexts: int = 1):
+        h = ctypes.c_void_p()
+        _check(_cb_create(nwaiters, ncontexts, ctypes.byref(h)), "counting_barrier_create")
+        self._h = h
+        self.nwaiters = nwaiters
+        self.ncontexts = ncontexts
+
+    def run(self, R: int, nsteps: int, ncontexts: int = 1, expected: int | None = None,
+            mode: str = "barrier", stream=None, **opts) -> None:
+        if expected is None:
+            expected = R - 1 if mode == "barrier" else 1
+        o = _options(sync=mode, **opts)
+        _check(_cb_run(self._h, R, nsteps, ncontexts, expected, ctypes.byref(o),
+                       _stream_handle(stream)), "counting_barrier_run")
+
+    def read(self, ctx: int, waiter: int):
+        v, s = _u64(), _u64()
+        _check(_cb_read(self._h, ctx, waiter, ctypes.byref(v), ctypes.byref(s)),
+               "counting_barrier_read")
+        return v.value, s.value
+
+    def reset(self, stream=None) -> None:
+        _check(_cb_reset(self._h, _stream_handle(stream)), "counting_barrier_reset")
+
+    def preset(self, value: int, stream=None) -> None:
+        _check(_cb_preset(self._h, value, _stream_handle(stream)), "counting_barrier_preset")
+
+    def close(self) -> None:
+        if self._h:
+            _check(_cb_destroy(self._h), "counting_barrier_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass
+class Slabs:
+    """R rank buffers carved from one allocation, each 16-byte aligned, with
+    guard words between them (so a stray write past a buffer is detectable)."""
+    storage: torch.Tensor
+    ranks: list
+    stride: int
+
+
+def make_slabs(R: int, count: int, dtype: torch.dtype, device="cuda", guard_bytes: int = 256,
+               fill=None) -> Slabs:
+    esize = torch.tensor([], dtype=dtype).element_size()
+    per = (count * esize + guard_bytes + 255) // 256 * 256 // esize  # elements per slab stride
+    storage = torch.empty(R * per + guard_bytes // esize, dtype=dtype, device=device)
+    if fill is not None:
+        storage.fill_(fill)
+    ranks = [storage[r * per: r * per + count] for r in range(R)]
+    return Slabs(storage, ranks, per)

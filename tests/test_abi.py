@@ -1,0 +1,136 @@
+"""The C-ABI library: it loads, exports what include/rr.h declares, and rejects
+bad arguments on the host before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rr.h")
+
+
+@pytest.fixture(scope="module")
+def rr():
+    import ring_allreduce_amd
+    return ring_allreduce_amd
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\**\s*([a-z_][a-z_0-9]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring",
+                     "counting_barrier_create", "counting_barrier_run", "counting_barrier_read",
+                     "counting_barrier_reset", "counting_barrier_destroy",
+                     "rr_last_kernel_error"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(rr):
+    names = _declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", rr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(rr.EXPORTED) == names
+    lib = ctypes.CDLL(rr.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings(rr):
+    assert rr.abi_version() == 1
+    for code, name in rr.STATUS.items():
+        assert rr.status_string(code).startswith(name)
+    assert "unknown" in rr.status_string(99)
+
+
+A = 0x7F0000000000  # 16-byte aligned addresses; never dereferenced by these tests
+
+
+@pytest.mark.parametrize("case", [
+    dict(ptrs=[], count=16),                                    # R = 0
+    dict(ptrs=[A + i * 4096 for i in range(65)], count=16),     # R = 65
+    dict(ptrs=[A, A + 4096], count=16, nslices=0),
+    dict(ptrs=[A, A + 4096], count=16, nslices=1025),
+    dict(ptrs=[A, A + 4096], count=16, dtype=7),
+    dict(ptrs=[A, A + 4096], count=16, op=5),
+    dict(ptrs=[A, A + 4104], count=16),                         # misaligned
+    dict(ptrs=[A, 0], count=16),                                # null buffer
+    dict(ptrs=[A, A + 32], count=16),                           # overlap (64 bytes each)
+    dict(ptrs=[A + 4096, A, A + 4096 + 16], count=8),           # overlap after sorting
+    dict(ptrs=[A, A + 4096], count=16, sync=9),
+    dict(ptrs=[A, A + 4096], count=16, block=128),
+    dict(ptrs=[A, A + 4096], count=16, team=-1),
+    dict(ptrs=[A, A + 4096], count=(1 << 40) + 1),
+])
+def test_invalid_arguments_rejected_on_host(rr, case):
+    kw = dict(case)
+    ptrs = kw.pop("ptrs")
+    count = kw.pop("count")
+    st = rr.allreduce_ring_ptrs(ptrs, count, kw.pop("dtype", "fp32"), kw.pop("op", "sum"),
+                                kw.pop("nslices", 1), **kw)
+    assert st == rr.RR_ERR_INVALID
+
+
+def test_null_buffer_array(rr):
+    st = rr._allreduce_ring(None, 4, 16, 1, 0, 1, None)
+    assert st == rr.RR_ERR_INVALID
+
+
+@pytest.mark.parametrize("phase", ["reduce_scatter", "all_gather"])
+def test_invalid_arguments_other_phases(rr, phase):
+    st = rr.allreduce_ring_ptrs([A, A + 8], 16, "fp32", "sum", 1, phase=phase)
+    assert st == rr.RR_ERR_INVALID
+
+
+def test_trivial_calls_are_no_ops(rr):
+    # one rank, or nothing to reduce: success without any device work
+    assert rr.allreduce_ring_ptrs([A], 1 << 20, "fp32") == rr.RR_OK
+    assert rr.allreduce_ring_ptrs([A, A + 4096], 0, "bf16") == rr.RR_OK
+
+
+def test_counting_barrier_rejects_bad_shapes(rr):
+    h = ctypes.c_void_p()
+    assert rr._cb_create(0, 1, ctypes.byref(h)) == rr.RR_ERR_INVALID
+    assert rr._cb_create(65, 1, ctypes.byref(h)) == rr.RR_ERR_INVALID
+    assert rr._cb_create(4, 0, ctypes.byref(h)) == rr.RR_ERR_INVALID
+    assert rr._cb_create(4, 1025, ctypes.byref(h)) == rr.RR_ERR_INVALID
+    assert rr._cb_create(4, 1, None) == rr.RR_ERR_INVALID
+    assert rr._cb_destroy(None) == rr.RR_OK
+    assert rr._cb_run(None, 4, 1, 1, 3, None, None) == rr.RR_ERR_INVALID
+
+
+def test_copy_rejects_bad_arguments(rr):
+    assert rr._hbm_copy(None, A, 16, None) == rr.RR_ERR_INVALID
+    assert rr._hbm_copy(A + 8, A + 4096, 16, None) == rr.RR_ERR_INVALID
+    assert rr._hbm_copy(A, A + 8, 64, None) in (rr.RR_ERR_INVALID,)
+    assert rr._hbm_copy(A, A + 4096, 0, None) == rr.RR_OK
+
+
+def test_plan_query_rejects_bad_arguments(rr):
+    p = rr._Plan()
+    assert rr._plan_query(0, 16, 1, 1, 0, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
+    assert rr._plan_query(4, 16, 1, 1, 3, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
+    assert rr._plan_query(4, 16, 1, 1, 0, None, None) == rr.RR_ERR_INVALID
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The GPU library and its binding never reach into the oracle."""
+    pkg = os.path.join(ROOT, "ring_allreduce_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.lower(), f
+    out = subprocess.run(["ldd", os.path.join(pkg, "librr.so")], capture_output=True, text=True).stdout
+    assert "ring_oracle" not in out

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP ring kernels against the CPU oracle, element by element.
+
+Small and multi-tile sizes are compared in full (every element of every rank,
+guard bands included); the full-size workloads are checked at sampled positions
+the oracle computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import (assert_matches_oracle, bits_equal, guards_intact, log, oracle_at,
+                            oracle_expect, sample_positions, to_host, to_slabs)
+
+pytestmark = pytest.mark.gpu
+
+DIST = {"int32": "int_pm1000", "fp32": "uniform_pm1", "bf16": "normal"}
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_allreduce_amd
+    ring_allreduce_amd.init()
+    return ring_allreduce_amd
+
+
+def run_case(rr, x, dtype, op, nslices, phase="allreduce", **opts):
+    R, count = len(x), x[0].size
+    slabs = to_slabs(rr, x, dtype)
+    if phase == "allreduce":
+        rr.allreduce_ring(slabs.ranks, op, nslices, **opts)
+    elif phase == "reduce_scatter":
+        rr.reduce_scatter_ring(slabs.ranks, op, nslices, **opts)
+    else:
+        rr.all_gather_ring(slabs.ranks, nslices, **opts)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(slabs, dtype, count), "a kernel wrote outside the rank buffers"
+    return [to_host(t, dtype) for t in slabs.ranks]
+
+
+# ----------------------------------------------------------- worked example
+
+@pytest.mark.parametrize("sync", ["auto", "p2p", "barrier", "launch"])
+def test_worked_example(rr, sync):
+    w = workloads.WORKED_EXAMPLE
+    log(f"case worked_example sync={sync}")
+    x = workloads.inputs(w)
+    got = run_case(rr, x, w.dtype, w.op, w.nslices, sync=sync)
+    assert_matches_oracle(got, oracle_expect(x, w.op), w.dtype, "worked example")
+
+
+# ------------------------------------------------------------ small, ragged
+
+SMALL = [
+    # R, count, nslices, team
+    (2, 37, 1, 1), (3, 1000, 2, 1), (4, 4 * 4 * 7 + 3, 3, 2), (5, 12345, 4, 3),
+    (8, 8 * 1024 + 5, 4, 2), (16, 16 * 8 * 33 + 7, 5, 1), (7, 6, 1, 1), (13, 9999, 16, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("int32", "max"), ("fp32", "sum"),
+                                      ("fp32", "max"), ("bf16", "sum"), ("bf16", "max")])
+@pytest.mark.parametrize("R,count,nslices,team", SMALL)
+@pytest.mark.parametrize("sync", ["p2p", "barrier", "launch"])
+def test_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
+    log(f"case small {dtype} {op} R={R} count={count} ns={nslices} team={team} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], R * 31 + count % 97)
+    got = run_case(rr, x, dtype, op, nslices, sync=sync, team=team)
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"R={R} count={count}")
+
+
+# ----------------------------------------------- several tiles, default plan
+
+MULTI = [(8, "fp32", "sum", (1 << 20) + 13, 4), (8, "bf16", "sum", (1 << 21) + 9, 8),
+         (16, "fp32", "max", (1 << 20) + 3, 16), (4, "int32", "sum", 3 << 19, 2),
+         (64, "fp32", "sum", 64 * 4096 + 5, 8)]
+
+
+@pytest.mark.parametrize("R,dtype,op,count,nslices", MULTI)
+@pytest.mark.parametrize("sync", ["auto", "barrier"])
+def test_multi_tile(rr, R, dtype, op, count, nslices, sync):
+    p = rr.plan(R, count, dtype, nslices, sync=sync)
+    log(f"case multi R={R} {dtype} {op} count={count} ns={nslices} sync={sync} plan={p}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], 100 + R)
+    got = run_case(rr, x, dtype, op, nslices, sync=sync)
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"multi R={R}")
+
+
+# ------------------------------------------------- the phases on their own
+
+@pytest.mark.parametrize("dtype,op", [("fp32", "sum"), ("bf16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("R", [2, 5, 8])
+@pytest.mark.parametrize("sync", ["auto", "launch"])
+def test_reduce_scatter_state(rr, dtype, op, R, sync):
+    """Every chunk of every rank after ReduceScatter, partials included."""
+    count = R * 3000 + 11
+    log(f"case reduce_scatter {dtype} {op} R={R} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], 5 + R)
+    got = run_case(rr, x, dtype, op, 3, phase="reduce_scatter", sync=sync)
+    assert_matches_oracle(got, oracle_expect(x, op, "reduce_scatter"), dtype, "reduce_scatter")
+
+
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+@pytest.mark.parametrize("R", [2, 3, 8])
+def test_all_gather_is_bitwise(rr, dtype, R):
+    """Random bit patterns, NaN payloads included, are copied untouched."""
+    count = R * 2048 + 5
+    log(f"case all_gather bits {dtype} R={R}")
+    x = workloads.generate(R, count, dtype, "bits", 77 + R)
+    got = run_case(rr, x, dtype, "sum", 4, phase="all_gather")
+    expect = oracle_expect(x, "sum", "all_gather")
+    for r in range(R):
+        assert np.array_equal(got[r].view(np.uint8), expect[r].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_reduce_scatter_then_all_gather(rr, dtype):
+    R, count = 8, 8 * 10000 + 3
+    log(f"case rs+ag {dtype}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], 3)
+    slabs = to_slabs(rr, x, dtype)
+    rr.reduce_scatter_ring(slabs.ranks, "sum", 4)
+    rr.all_gather_ring(slabs.ranks, 4)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    got = [to_host(t, dtype) for t in slabs.ranks]
+    assert_matches_oracle(got, oracle_expect(x, "sum"), dtype, "rs+ag")
+
+
+# -------------------------------------------------------------- invariance
+
+def test_invariance_across_slices_modes_teams(rr):
+    """Slices, sync modes, teams and block sizes only schedule: bits never change."""
+    R, count, dtype = 8, (1 << 18) + 17, "bf16"
+    x = workloads.generate(R, count, dtype, "normal", 12)
+    ref = None
+    for nslices in (1, 2, 4, 8, 16):
+        for sync in ("p2p", "barrier", "launch"):
+            for team, block in ((1, 256), (4, 512), (0, 1024)):
+                log(f"case invariance ns={nslices} sync={sync} team={team} block={block}")
+                got = run_case(rr, x, dtype, "sum", nslices, sync=sync, team=team, block=block)
+                if ref is None:
+                    ref = got
+                    assert_matches_oracle(got, oracle_expect(x, "sum"), dtype, "invariance")
+                else:
+                    for r in range(R):
+                        assert np.array_equal(got[r], ref[r])
+
+
+def test_repeat_runs_identical(rr):
+    R, count, dtype = 16, 16 * 40000 + 1, "fp32"
+    x = workloads.generate(R, count, dtype, "uniform_pm1", 4)
+    expect = oracle_expect(x, "sum")
+    slabs = to_slabs(rr, x, dtype)
+    pristine = slabs.storage.clone()
+    for k in range(10):
+        log(f"case repeat {k}")
+        slabs.storage.copy_(pristine)
+        rr.allreduce_ring(slabs.ranks, "sum", 4)
+        torch.cuda.synchronize()
+        rr.check_kernel_error()
+        got = [to_host(t, dtype) for t in slabs.ranks]
+        assert_matches_oracle(got, expect, dtype, f"repeat {k}")
+
+
+def test_no_xcd_map_and_cooperative(rr):
+    R, count, dtype = 8, 8 * 50000 + 9, "fp32"
+    x = workloads.generate(R, count, dtype, "uniform_pm1", 8)
+    expect = oracle_expect(x, "sum")
+    for flags in (rr.FLAG_NO_XCD_MAP, rr.FLAG_COOPERATIVE, 0):
+        log(f"case flags={flags}")
+        got = run_case(rr, x, dtype, "sum", 8, sync="p2p", flags=flags)
+        assert_matches_oracle(got, expect, dtype, f"flags {flags}")
+
+
+def test_separate_allocations(rr):
+    """Rank buffers need not share one allocation."""
+    R, count = 6, 6 * 7777 + 2
+    x = workloads.generate(R, count, "fp32", "uniform_pm1", 2)
+    ts = [torch.from_numpy(a).cuda() for a in x]
+    log("case separate allocations")
+    rr.allreduce_ring(ts, "sum", 2)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    expect = oracle_expect(x, "sum")
+    assert_matches_oracle([t.cpu().numpy() for t in ts], expect, "fp32", "separate")
+
+
+def test_edge_cases(rr):
+    log("case edge: R=1, count=0, count<R")
+    x = torch.randn(100, device="cuda")
+    y = x.clone()
+    rr.allreduce_ring([x], "sum", 1)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    e = [torch.empty(0, device="cuda") for _ in range(4)]
+    rr.allreduce_ring(e, "sum", 1)
+    xs = workloads.generate(8, 3, "int32", "int_pm1000", 1)
+    got = run_case(rr, xs, "int32", "sum", 4)
+    assert_matches_oracle(got, oracle_expect(xs, "sum"), "int32", "count<R")
+
+
+def test_tracers(rr):
+    R, count = 16, 16 * 4 * 9 + 1
+    log("case tracers")
+    x = workloads.generate(R, count, "int32", "onehot", 0)
+    got = run_case(rr, x, "int32", "sum", 3)
+    for g in got:
+        assert np.all(g.view(np.int32) == (1 << R) - 1)
+    x = workloads.generate(R, count, "int32", "rank", 0)
+    got = run_case(rr, x, "int32", "max", 3)
+    for g in got:
+        assert np.all(g.view(np.int32) == R - 1)
+
+
+def test_rolling_counters_near_wrap(rr):
+    """Signals and shadows preset just below 2^64 must keep working past the wrap."""
+    R, count = 8, 8 * 20000 + 3
+    x = workloads.generate(R, count, "fp32", "uniform_pm1", 9)
+    expect = oracle_expect(x, "sum")
+    rr.workspace_preset((1 << 64) - 3)
+    for sync in ("p2p", "barrier"):
+        log(f"case wrap sync={sync}")
+        got = run_case(rr, x, "fp32", "sum", 4, sync=sync)
+        assert_matches_oracle(got, expect, "fp32", f"wrap {sync}")
+    rr.workspace_preset(0)
+    torch.cuda.synchronize()
+
+
+def test_invalid_device_pointers_rejected(rr):
+    """A host pointer or a buffer running past its allocation never reaches a kernel."""
+    a = torch.zeros(1024, device="cuda")
+    b = torch.zeros(1024, device="cuda")
+    host = np.zeros(1024, dtype=np.float32)
+    st = rr.allreduce_ring_ptrs([a.data_ptr(), host.ctypes.data], 1024, "fp32")
+    assert st == rr.RR_ERR_INVALID
+    big = torch.zeros(4096, device="cuda")
+    tail = big.data_ptr() + (4096 - 256) * 4  # 256 floats left in its allocation
+    st = rr.allreduce_ring_ptrs([a.data_ptr(), b.data_ptr(), tail], 1024, "fp32")
+    # torch's caching allocator may place other tensors after `big`; the extent
+    # check is against the allocation, so either outcome is safe here
+    assert st in (rr.RR_OK, rr.RR_ERR_INVALID)
+    torch.cuda.synchronize()
+
+
+# -------------------------------------------------------- full-size workloads
+
+def _full_size(rr, w, n_random, opts=None):
+    opts = opts or {}
+    p = rr.plan(w.R, w.count, w.dtype, w.nslices, sync=w.sync, **opts)
+    log(f"case full {w.name} R={w.R} {w.dtype} {w.op} count={w.count} ns={w.nslices} "
+        f"sync={w.sync} plan={p}")
+    x = workloads.inputs(w)
+    slabs = to_slabs(rr, x, w.dtype, guard=True)
+    rr.allreduce_ring(slabs.ranks, w.op, w.nslices, sync=w.sync, **opts)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(slabs, w.dtype, w.count)
+    # property: every rank holds the same bits
+    raw = [t.view(torch.int32 if w.dtype != "bf16" else torch.int16) for t in slabs.ranks]
+    for r in range(1, w.R):
+        assert torch.equal(raw[r], raw[0]), f"rank {r} differs from rank 0"
+    # sampled positions against the oracle
+    pos = sample_positions(w.count, w.R, w.dtype, w.nslices, p, n_random, w.seed)
+    idx = torch.from_numpy(pos).cuda()
+    got = np.stack([to_host(t.index_select(0, idx), w.dtype) for t in slabs.ranks], axis=1)
+    want = oracle_at(x, pos, w.dtype, w.op)
+    eq = bits_equal(got, want.view(got.dtype), w.dtype)
+    assert eq.all(), f"{np.count_nonzero(~eq)} of {eq.size} sampled results differ"
+    # property: within the error bound of the order-free fp64 sum (floating point SUM)
+    if w.op == "sum" and w.dtype != "int32":
+        sub = [a[pos] for a in x]
+        d, mag = oracle.direct_sum_f64(sub)
+        y = got[:, 0]
+        yv = (y.astype(np.uint32) << 16).view(np.float32) if w.dtype == "bf16" else y.view(np.float32)
+        u = 2.0 ** -24 if w.dtype == "fp32" else 2.0 ** -8
+        gamma = (w.R - 1) * u / (1 - (w.R - 1) * u)
+        err = np.abs(yv.astype(np.float64) - d)
+        assert np.all(err <= gamma * mag * (1 + 1e-12))
+        if w.dtype == "fp32":
+            assert np.all(err <= 1e-5 * mag)
+        else:
+            assert np.linalg.norm(yv - d) <= 1e-2 * np.linalg.norm(d)
+    del slabs
+    torch.cuda.empty_cache()
+
+
+def test_full_r8_fp32_64MiB(rr):
+    _full_size(rr, workloads.R8_FP32_64MIB, 20000)
+
+
+def test_full_r8_bf16_256MiB(rr):
+    _full_size(rr, workloads.R8_BF16_256MIB, 20000)
+
+
+def test_full_r64_fp32_32MiB(rr):
+    _full_size(rr, workloads.R64_FP32_32MIB, 3000)
+
+
+@pytest.mark.parametrize("k", range(0, 9))
+def test_full_r16_sweep(rr, k):
+    for op, ns in (("sum", 16), ("max", 1 + (k % 4) * 5)):
+        _full_size(rr, workloads.r16_sweep(k, op, ns), 4000)
