@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--barrier-latency", action="store_true",
+                    help="instead of the AllReduce: per-step latency of the counting barrier "
+                         "alone for R = 2..64 and 1 or 8 contexts (one JSON line per point)")
     return ap.parse_args()
 
 
@@ -109,6 +112,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.barrier_latency:
+        return barrier_latency(rr, torch)
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
@@ -233,6 +238,46 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
     }
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def barrier_latency(rr, torch):
+    """Per-step latency of the counting barrier on its own: one 64-lane workgroup per
+    (context, waiter); per step each waiter arrives (adds 1 to the other R-1
+    waiters' signals, or to its successor's in p2p mode) and waits for its own
+    signal to advance by the expected count.  us/step = (t(nsteps) - t(0)) / nsteps,
+    best of 5 timed launches each."""
+    rr.init()
+    b = rr.CountingBarrier(64, 8)
+    stream = torch.cuda.current_stream()
+
+    def timed(R, nsteps, nctx, mode):
+        best = None
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.run(R, nsteps, nctx, mode=mode)
+            e.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(e)
+            best = ms if best is None else min(best, ms)
+        rr.check_kernel_error()
+        return best
+
+    steps = 2000
+    for mode in ("barrier", "p2p"):
+        for nctx in (1, 8):
+            for R in (2, 4, 8, 16, 32, 64):
+                b.run(R, 100, nctx, mode=mode)  # warm
+                t0 = timed(R, 0, nctx, mode)
+                t1 = timed(R, steps, nctx, mode)
+                us = (t1 - t0) * 1e3 / steps
+                print(json.dumps({"metric": "counting barrier latency per step", "mode": mode,
+                                  "R": R, "contexts": nctx, "us_per_step": round(us, 3),
+                                  "atomics_per_step": nctx * R * ((R - 1) if mode == "barrier" else 1),
+                                  "empty_launch_ms": round(t0, 4)}), flush=True)
+    b.close()
     return 0
 
 

@@ -109,7 +109,8 @@ typedef enum {
 #define RR_INJECT_DROP_ARRIVAL   0x2u /* rank 0, context 0 skips its first arrival */
 
 /* Flags. */
-#define RR_FLAG_NO_XCD_MAP       0x1u /* plain block -> (rank, slice) order */
+#define RR_FLAG_NO_XCD_MAP       0x1u /* plain block -> (rank, lane) order; hand-offs then
+                                         cross XCDs and write L2 back every hop */
 #define RR_FLAG_NO_POINTER_CHECK 0x2u /* skip the per-call allocation-extent check */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
@@ -121,10 +122,14 @@ typedef struct {
     int32_t sync;        /* rr_sync_t */
     int32_t team;        /* workgroups per (rank, slice); 0 = choose */
     int32_t block;       /* threads per workgroup: 0 (= 512), 256, 512 or 1024 */
-    int32_t reserved;
+    int32_t rounds;      /* lane groups each workgroup runs one after another
+                            (depth * rounds must divide slices * team);
+                            0 = choose from the buffer size */
     uint64_t timeout_ns; /* bound on every device wait; 0 = 2 s */
     uint32_t inject;     /* RR_INJECT_* */
     uint32_t flags;      /* RR_FLAG_* */
+    int32_t depth;       /* lanes each workgroup interleaves hop by hop, 1..4; 0 = choose */
+    int32_t reserved;
 } rr_options_t;
 
 /* What a call will run (rr_plan_query). */
@@ -134,9 +139,12 @@ typedef struct {
     int32_t block;
     int32_t grid;        /* workgroups per launch */
     int32_t launches;    /* kernel launches per call */
-    int32_t xcd_map;     /* 1 if a slice's ranks share one XCD */
+    int32_t xcd_map;     /* 1 if each column of R workgroups is placed on one XCD
+                            (the grid is then padded to a multiple of 8 columns) */
     int32_t cooperative; /* 1 if launched with hipLaunchCooperativeKernel */
     int32_t resident_max;/* workgroups the device can hold at once for this kernel */
+    int32_t rounds;      /* lane groups each workgroup runs one after another */
+    int32_t depth;       /* lanes each workgroup interleaves */
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */
     uint64_t sub_len;    /* elements per team member */

@@ -52,15 +52,17 @@ ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
 
 class Options(ctypes.Structure):
     _fields_ = [("sync", ctypes.c_int32), ("team", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
-                ("inject", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+                ("rounds", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
+                ("inject", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("depth", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [("sync", ctypes.c_int32), ("team", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("xcd_map", ctypes.c_int32), ("cooperative", ctypes.c_int32),
-                ("resident_max", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
+                ("resident_max", ctypes.c_int32), ("rounds", ctypes.c_int32),
+                ("depth", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
                 ("slice_len", ctypes.c_uint64), ("sub_len", ctypes.c_uint64),
                 ("hbm_bytes", ctypes.c_uint64)]
 
@@ -153,9 +155,9 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
-def _options(sync="auto", team=0, block=0, timeout_ns=0, inject=0, flags=0):
-    return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, 0,
-                   timeout_ns, inject, flags)
+def _options(sync="auto", team=0, block=0, rounds=0, timeout_ns=0, inject=0, flags=0, depth=0):
+    return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, rounds,
+                   timeout_ns, inject, flags, depth, 0)
 
 
 def _buffers(tensors):

@@ -42,8 +42,18 @@
 namespace rr {
 
 constexpr int kMaxDevices = 64;
+constexpr int kMaxDepth = 4;
 constexpr int kSlots = RR_MAX_SLICES * RR_MAX_RANKS;  // (context, rank) pairs
 constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
+// Bytes one hop of the lanes in flight may move before a partial written in
+// that hop risks leaving the 256 MB Infinity Cache before it is read back.
+constexpr uint64_t kRoundBytes = 192ull << 20;
+// Lanes a workgroup interleaves when the caller does not choose: a per-hop
+// barrier waits for the slowest of R workgroups, which a second lane hides; a
+// predecessor hand-off is cheap enough that a second lane costs more than it
+// hides (measured on MI355X).
+constexpr int kAutoDepthBarrier = 2;
+constexpr int kAutoDepthP2P = 1;
 
 struct RingArgs {
     void* bufs[RR_MAX_RANKS];
@@ -65,7 +75,9 @@ struct RingArgs {
     int32_t sync;        // SYNC_NONE (one hop per launch), SYNC_P2P, SYNC_BARRIER
     int32_t xcd_map;
     uint32_t inject;
-    int32_t pad;
+    int32_t cols;        // workgroups per rank = grid / R
+    int32_t rounds;      // lane groups each workgroup runs one after another
+    int32_t depth;       // lanes each workgroup interleaves hop by hop (1..kMaxDepth)
 };
 
 __device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -75,9 +87,25 @@ __device__ __forceinline__ int wrap(int a, int m) {
     return r < 0 ? r + m : r;
 }
 
-// Workgroup index of (rank k, lane) -- the inverse of the decoding in ring_kernel.
-__device__ __forceinline__ int block_of(int k, int lane, int R, bool xcd_map) {
-    return xcd_map ? ((lane >> 3) * R + k) * 8 + (lane & 7) : lane * R + k;
+// Workgroups are dealt to the 8 XCDs round-robin by index.  Both kernels lay
+// their grid out as columns of R workgroups (one per rank) with every column on
+// one XCD: block b = ((col / 8) * R + rank) * 8 + col % 8.  Column counts are
+// padded to a multiple of 8; padding columns exit at once.
+struct Place {
+    int rank;
+    int col;
+};
+
+__device__ __forceinline__ Place place_of(int b, int R, bool xcd_map) {
+    if (xcd_map) {
+        const int x = b & 7, k = b >> 3;
+        return {k % R, (k / R) * 8 + x};
+    }
+    return {b % R, b / R};
+}
+
+__device__ __forceinline__ int block_of(int rank, int col, int R, bool xcd_map) {
+    return xcd_map ? ((col >> 3) * R + rank) * 8 + (col & 7) : col * R + rank;
 }
 
 // The XCD (accelerator complex die) this wave runs on.
@@ -85,25 +113,33 @@ __device__ __forceinline__ uint32_t xcc_id() {
     return __builtin_amdgcn_s_getreg(20 /* HW_REG_XCC_ID */ | (0 << 6) | ((4 - 1) << 11));
 }
 
-// Called by wave 0.  True when all R workgroups of `lane` run on this
-// workgroup's XCD, read from the table every workgroup fills at start; such a
-// lane shares one L2, which then is the point where producer stores and
-// consumer loads meet.  Every workgroup of the lane computes the same answer.
-// Returns -1 if a lane-mate never published (timeout or a failure elsewhere).
-__device__ int lane_on_one_xcd(const RingArgs& a, int lane, uint32_t mine) {
+// Every synchronising workgroup publishes (generation << 8) | XCC id at start.
+__device__ __forceinline__ void publish_xcc(uint64_t* table, uint32_t generation, uint32_t xcc) {
+    __hip_atomic_store(&table[blockIdx.x], ((uint64_t)generation << 8) | xcc, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by wave 0.  1 when the R workgroups of column `col` all run on this
+// workgroup's XCD (read from the published table), 0 if not; they then share one
+// L2, the point where producer stores and consumer loads meet.  All R
+// workgroups of the column compute the same answer.  -1 if one never published
+// (timeout, or a failure elsewhere).
+__device__ int column_on_one_xcd(const uint64_t* table, uint32_t generation, int R, int col,
+                                 bool xcd_map, uint32_t mine, const ErrorRecord* err,
+                                 uint64_t timeout_ticks) {
     const int k = threadIdx.x;
     int same = 1;
     int failed = 0;
-    if (k < a.R) {
-        const uint64_t* e = &a.xcc_table[block_of(k, lane, a.R, a.xcd_map != 0)];
+    if (k < R) {
+        const uint64_t* e = &table[block_of(k, col, R, xcd_map)];
         uint64_t v = sig_read(e);
         const uint64_t start = wall_clock64();
         uint32_t spins = 0;
-        while ((uint32_t)(v >> 8) != a.generation) {
+        while ((uint32_t)(v >> 8) != generation) {
             __builtin_amdgcn_s_sleep(1);
             v = sig_read(e);
             if ((++spins & 31u) == 0u &&
-                (sig_read(&a.err->flag) != 0 || wall_clock64() - start > a.timeout_ticks)) {
+                (sig_read(&err->flag) != 0 || wall_clock64() - start > timeout_ticks)) {
                 failed = 1;
                 break;
             }
@@ -114,178 +150,250 @@ __device__ int lane_on_one_xcd(const RingArgs& a, int lane, uint32_t mine) {
     return __all(same) ? 1 : 0;
 }
 
+// Producer side of a hand-off, executed by every thread of the workgroup
+// before its barrier and arrival.  Same XCD: each wave waits until its stores
+// have reached the shared L2.  Otherwise, also write the L2 back so that other
+// XCDs see the stores -- once per workgroup, after every wave's stores are in L2.
+__device__ __forceinline__ void release_stores(bool local) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!local) {
+        __syncthreads();
+        if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+}
+
+// Consumer side, executed by the one thread that saw the signal, before the
+// workgroup barrier.  Same XCD: nothing to invalidate -- incoming data are read
+// with device-scope loads that skip the L1 and meet the producer's stores in the
+// shared L2 (a workgroup-scope L1 invalidate would not do: outside
+// thread-group-split mode the L1 counts as coherent for one workgroup and is left
+// alone).  Otherwise: an agent-scope acquire (L1 and L2 invalidate), completed
+// before any wave loads.
+__device__ __forceinline__ void acquire_stores(bool local) {
+    if (local) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
+
+// Loads of the incoming buffer -- data another workgroup wrote earlier in this
+// launch -- go through a buffer descriptor with device-scope coherence (sc1):
+// they skip this CU's L1, which may still hold lines of the same addresses from
+// an earlier hop (a workgroup reads a chunk's partial in ReduceScatter and its
+// finished value one AllGather hop later), and are served by the L2.  Within one
+// XCD that L2 already holds the producer's stores, so the consumer needs no
+// cache invalidation at all.  The descriptor also bounds every load: a load
+// outside [base, base + bytes) returns zero instead of touching memory.
+constexpr int kAuxDeviceScope = 16;             // sc1
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw (untyped) buffer access on gfx9
+constexpr uint64_t kPieceBytes = 1ull << 30;    // one descriptor covers at most this
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t incoming(const void* base, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load_in(__amdgpu_buffer_rsrc_t rs, uint32_t vec) {
+    return __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(vec * 16u), 0, kAuxDeviceScope));
+}
+
 // One hop of one workgroup over elements [lo, hi) of both buffers.  ReduceScatter:
 // dst = fold(src, dst).  AllGather: dst = src, bit for bit.  16-byte vectors,
 // U vectors per thread in flight, then a scalar tail (only at the ragged end).
 template <int DT, int OP, int BLOCK, int U>
-__device__ __forceinline__ void hop_body(bool reduce, const void* srcbuf, void* dstbuf,
-                                         uint64_t lo, uint64_t hi) {
+__device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void* dstbuf,
+                                          uint64_t lo, uint64_t hi) {
     constexpr int ES = ElemBytes<DT>::value;
     constexpr int V = 16 / ES;
     const uint64_t n = hi - lo;
     const uint32_t nv = (uint32_t)(n / V);
-    const u32x4* __restrict__ s = (const u32x4*)((const char*)srcbuf + lo * ES);
+    const char* sb = (const char*)srcbuf + lo * ES;
+    const __amdgpu_buffer_rsrc_t rs = incoming(sb, n * ES);
     u32x4* __restrict__ d = (u32x4*)((char*)dstbuf + lo * ES);
     uint32_t i = threadIdx.x;
     if (reduce) {
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) x[u] = s[i + u * BLOCK];
+            for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
 #pragma unroll
             for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
 #pragma unroll
             for (int u = 0; u < U; ++u) d[i + u * BLOCK] = fold4<DT, OP>(x[u], y[u]);
         }
-        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(s[i], d[i]);
+        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(load_in(rs, i), d[i]);
     } else {
         constexpr int UC = 2 * U;
         for (; i + (UC - 1) * BLOCK < nv; i += UC * BLOCK) {
             u32x4 x[UC];
 #pragma unroll
-            for (int u = 0; u < UC; ++u) x[u] = s[i + u * BLOCK];
+            for (int u = 0; u < UC; ++u) x[u] = load_in(rs, i + u * BLOCK);
 #pragma unroll
             for (int u = 0; u < UC; ++u) d[i + u * BLOCK] = x[u];
         }
-        for (; i < nv; i += BLOCK) d[i] = s[i];
+        for (; i < nv; i += BLOCK) d[i] = load_in(rs, i);
     }
     const uint64_t t = (uint64_t)nv * V + threadIdx.x;  // fewer than V elements remain
     if (t < n) {
-        const char* sp = (const char*)srcbuf + (lo + t) * ES;
         char* dp = (char*)dstbuf + (lo + t) * ES;
-        if (reduce) {
-            fold_one<DT, OP>(sp, dp);
-        } else if (ES == 2) {
-            *(uint16_t*)dp = *(const uint16_t*)sp;
+        const int off = (int)(t * ES);
+        if constexpr (ES == 2) {
+            const uint16_t in =
+                __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kAuxDeviceScope);
+            if (reduce)
+                *(uint16_t*)dp = (uint16_t)Fold<DT, OP>::half(in, *(const uint16_t*)dp);
+            else
+                *(uint16_t*)dp = in;
         } else {
-            *(uint32_t*)dp = *(const uint32_t*)sp;
+            const uint32_t in = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kAuxDeviceScope);
+            if (reduce)
+                *(uint32_t*)dp = Fold<DT, OP>::lane(in, *(const uint32_t*)dp);
+            else
+                *(uint32_t*)dp = in;
         }
     }
+}
+
+template <int DT, int OP, int BLOCK, int U>
+__device__ __forceinline__ void hop_body(bool reduce, const void* srcbuf, void* dstbuf,
+                                         uint64_t lo, uint64_t hi) {
+    constexpr uint64_t kPiece = kPieceBytes / ElemBytes<DT>::value;  // elements, vector multiple
+    for (uint64_t p = lo; p < hi; p += kPiece)
+        hop_piece<DT, OP, BLOCK, U>(reduce, srcbuf, dstbuf, p, umin(p + kPiece, hi));
 }
 
 template <int DT, int OP, int BLOCK>
 __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
     constexpr int U = 4;
     const int R = a.R;
-    int r, lane;
-    if (a.xcd_map) {
-        // Workgroups are dealt to the 8 XCDs round-robin by index; keep all R
-        // ranks of a lane (slice j, member w) on one XCD so each hand-off stays
-        // inside one L2.
-        const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-        r = k % R;
-        lane = (k / R) * 8 + x;
-    } else {
-        r = blockIdx.x % R;
-        lane = blockIdx.x / R;
-    }
-    const int j = lane / a.team;
-    const int w = lane - j * a.team;
+    const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
+    const int r = pl.rank, col = pl.col;
+    if (col >= a.cols) return;  // padding column
     const int succ = r + 1 == R ? 0 : r + 1;
     const bool synced = a.g_last > a.g_first;
-    const int my_slot = lane * R + r;
 
     __shared__ int s_stop;
     __shared__ int s_local;
-    uint64_t shadow = 0;
     const uint32_t my_xcc = xcc_id() & 0xFu;
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;  // a recorded failure is sticky
-        if (synced) {
-            shadow = a.shadow[my_slot];
-            __hip_atomic_store(&a.xcc_table[blockIdx.x], ((uint64_t)a.generation << 8) | my_xcc,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (synced) publish_xcc(a.xcc_table, a.generation, my_xcc);
     }
     __syncthreads();
     if (s_stop) return;
-    // Producer side of the hand-off, fixed at the first hand-off of the launch:
-    // local -- all R workgroups of the lane run on one XCD and so share its L2,
-    //          the point where their loads and stores meet: each wave only waits
-    //          until its stores have reached L2;
-    // else  -- each wave makes its stores visible device-wide (agent-scope
-    //          release: an L2 write-back), as a consumer may sit on another XCD.
-    // The consumer side is the same in both cases: after the wait, one wave
-    // performs an agent-scope acquire, which also invalidates the CU's L1.  That
-    // matters even within one XCD: a workgroup re-reads a chunk of its incoming
-    // buffer (the partial in ReduceScatter, the finished chunk one AllGather hop
-    // later), and a workgroup-scope invalidate leaves the L1 copy in place.
+    // Producer side of the hand-off (release_stores), fixed at the first
+    // hand-off of the launch: `local` when all R workgroups of the column run on
+    // one XCD and so share its L2.  The consumer side (acquire_stores) is the
+    // same either way; its L1 invalidation matters even within one XCD, because a
+    // workgroup re-reads a chunk of its incoming buffer (the partial in
+    // ReduceScatter, the finished chunk one AllGather hop later).
     bool local = false;
+    bool decided = false;
     const uint64_t arrivals = a.sync == SYNC_BARRIER ? (uint64_t)(R - 1) : 1;
-    const bool injected = r == 0 && lane == 0;
+    __shared__ int s_stop_lane[kMaxDepth];
 
-    // this workgroup's element range, relative to the start of any chunk
-    const uint64_t off_lo = (uint64_t)j * a.slice_len + (uint64_t)w * a.sub_len;
-    const uint64_t off_hi =
-        umin(off_lo + a.sub_len, umin((uint64_t)(j + 1) * a.slice_len, a.chunk_len));
-
-    for (int g = a.g_first; g <= a.g_last; ++g) {
-        if (g > a.g_first) {
-            if (threadIdx.x == 0) {
-                uint64_t target = shadow + arrivals;
-                if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected && g == a.g_first + 1)
-                    target += 1;
-                const WaitResult res = sig_wait(&a.sig[(uint64_t)my_slot * kSignalStride], target,
-                                                a.err, a.timeout_ticks);
-                if (res.status == WAIT_TIMEOUT)
-                    record_timeout(a.err, lane, r, g, target, res.observed);
-                shadow = target;
-                s_stop = res.status != WAIT_OK;
-                // Acquire for the whole workgroup: drop this CU's L1 copies (and
-                // non-coherent L2 lines), and finish that before any wave loads.
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-            __syncthreads();
-            if (s_stop) return;
+    // Lane groups one after another: only cols * depth lanes are in flight at
+    // once, so the partial a hop writes is still cached when the next hop reads
+    // it, whatever the buffer size.  Within a group the workgroup interleaves its
+    // `depth` lanes hop by hop -- hop g of lane 1 runs while lane 0's hand-off
+    // for hop g+1 completes.  Every wait targets a (lane, hop) that comes earlier
+    // in the (hop, lane) order all workgroups follow, so the interleave cannot
+    // deadlock.
+    for (int round = 0; round < a.rounds; ++round) {
+        int lane[kMaxDepth];
+        uint64_t off_lo[kMaxDepth], off_hi[kMaxDepth], shadow[kMaxDepth];
+#pragma unroll
+        for (int p = 0; p < kMaxDepth; ++p) {
+            lane[p] = col + (round * a.depth + p) * a.cols;
+            const int j = lane[p] / a.team;
+            const int w = lane[p] - j * a.team;
+            off_lo[p] = (uint64_t)j * a.slice_len + (uint64_t)w * a.sub_len;
+            off_hi[p] = umin(off_lo[p] + a.sub_len,
+                             umin((uint64_t)(j + 1) * a.slice_len, a.chunk_len));
+            shadow[p] = 0;
+            if (p < a.depth && synced && threadIdx.x == 0) shadow[p] = a.shadow[lane[p] * R + r];
         }
 
-        int c;
-        bool reduce;
-        if (g <= R - 1) {
-            c = wrap(r - g + 1, R);
-            reduce = true;
-        } else {
-            c = wrap(r + 2 - (g - (R - 1)), R);
-            reduce = false;
-        }
-        const uint64_t base = (uint64_t)c * a.chunk_len;
-        const uint64_t lo = base + off_lo;
-        const uint64_t hi = umin(base + off_hi, a.count);
-        if (lo < hi) hop_body<DT, OP, BLOCK, U>(reduce, a.bufs[r], a.bufs[succ], lo, hi);
-
-        if (g < a.g_last) {
-            if (g == a.g_first) {
-                if (threadIdx.x < 64) {
-                    const int v = lane_on_one_xcd(a, lane, my_xcc);
+        for (int g = a.g_first; g <= a.g_last; ++g) {
+#pragma unroll
+            for (int p = 0; p < kMaxDepth; ++p) {
+                if (p >= a.depth) break;
+                const int my_slot = lane[p] * R + r;
+                const bool injected = r == 0 && lane[p] == 0;
+                if (g > a.g_first) {
                     if (threadIdx.x == 0) {
-                        if (v < 0) record_timeout(a.err, lane, r, 0, a.generation, 0);
-                        s_local = v;
+                        uint64_t target = shadow[p] + arrivals;
+                        if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected &&
+                            g == a.g_first + 1)
+                            target += 1;
+                        const WaitResult res = sig_wait(&a.sig[(uint64_t)my_slot * kSignalStride],
+                                                        target, a.err, a.timeout_ticks);
+                        if (res.status == WAIT_TIMEOUT)
+                            record_timeout(a.err, lane[p], r, g, target, res.observed);
+                        shadow[p] = target;
+                        s_stop_lane[p] = res.status != WAIT_OK;
+                        acquire_stores(local);
+                    }
+                    __syncthreads();
+                    if (s_stop_lane[p]) return;
+                }
+
+                int c;
+                bool reduce;
+                if (g <= R - 1) {
+                    c = wrap(r - g + 1, R);
+                    reduce = true;
+                } else {
+                    c = wrap(r + 2 - (g - (R - 1)), R);
+                    reduce = false;
+                }
+                const uint64_t base = (uint64_t)c * a.chunk_len;
+                const uint64_t lo = base + off_lo[p];
+                const uint64_t hi = umin(base + off_hi[p], a.count);
+                if (lo < hi) hop_body<DT, OP, BLOCK, U>(reduce, a.bufs[r], a.bufs[succ], lo, hi);
+
+                if (g < a.g_last) {
+                    if (!decided) {
+                        if (threadIdx.x < 64) {
+                            const int v = column_on_one_xcd(a.xcc_table, a.generation, R, col,
+                                                            a.xcd_map != 0, my_xcc, a.err,
+                                                            a.timeout_ticks);
+                            if (threadIdx.x == 0) {
+                                if (v < 0) record_timeout(a.err, lane[p], r, 0, a.generation, 0);
+                                s_local = v;
+                            }
+                        }
+                        __syncthreads();
+                        if (s_local < 0) return;
+                        local = s_local == 1;
+                        decided = true;
+                    }
+                    release_stores(local);
+                    __syncthreads();
+                    const bool drop =
+                        (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && g == a.g_first;
+                    if (!drop) {
+                        if (a.sync == SYNC_BARRIER) {
+                            if ((int)threadIdx.x < R - 1) {
+                                const int q = wrap(r + 1 + (int)threadIdx.x, R);
+                                sig_add(&a.sig[(uint64_t)(lane[p] * R + q) * kSignalStride], 1);
+                            }
+                        } else if (threadIdx.x == 0) {
+                            sig_add(&a.sig[(uint64_t)(lane[p] * R + succ) * kSignalStride], 1);
+                        }
                     }
                 }
-                __syncthreads();
-                if (s_local < 0) return;
-                local = s_local == 1;
             }
-            if (local)
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores have reached L2
-            else
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
-            const bool drop = (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && g == a.g_first;
-            if (!drop) {
-                if (a.sync == SYNC_BARRIER) {
-                    if ((int)threadIdx.x < R - 1) {
-                        const int q = wrap(r + 1 + (int)threadIdx.x, R);
-                        sig_add(&a.sig[(uint64_t)(lane * R + q) * kSignalStride], 1);
-                    }
-                } else if (threadIdx.x == 0) {
-                    sig_add(&a.sig[(uint64_t)(lane * R + succ) * kSignalStride], 1);
-                }
-            }
+        }
+        if (synced && threadIdx.x == 0) {
+#pragma unroll
+            for (int p = 0; p < kMaxDepth; ++p)
+                if (p < a.depth) a.shadow[lane[p] * R + r] = shadow[p];  // sig == shadow again
         }
     }
-    if (synced && threadIdx.x == 0) a.shadow[my_slot] = shadow;  // sig == shadow again
 }
 
 // ---------------------------------------------------------- barrier only --
@@ -293,6 +401,7 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
 struct BarrierArgs {
     uint64_t* sig;
     uint64_t* shadow;
+    uint64_t* xcc_table;
     ErrorRecord* err;
     uint64_t timeout_ticks;
     uint64_t expected;  // arrivals per step
@@ -300,28 +409,41 @@ struct BarrierArgs {
     int32_t stride;     // waiters per context in the object's layout
     int32_t nsteps;
     int32_t mode;       // SYNC_P2P or SYNC_BARRIER
+    int32_t nctx;       // contexts taking part (columns; the grid is padded to 8)
+    uint32_t generation;
     uint32_t inject;
     int32_t pad;
 };
 
-// One 64-lane workgroup per (context, waiter).  Each step: release, arrive,
-// advance the shadow by `expected`, wait, acquire.
+// One 64-lane workgroup per (context, waiter), laid out like the ring kernel's
+// columns so a context's waiters share an XCD.  Each step: release, arrive,
+// advance the shadow by `expected`, wait, acquire -- the same hand-off the ring
+// kernel performs between hops, without the payload.
 __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
-    const int ctx = blockIdx.x / a.R;
-    const int r = blockIdx.x - ctx * a.R;
+    const Place pl = place_of(blockIdx.x, a.R, true);
+    const int r = pl.rank, ctx = pl.col;
+    if (ctx >= a.nctx || a.nsteps <= 0) return;
     const int slot = ctx * a.stride + r;
-    if (a.nsteps <= 0) return;
+    const uint32_t my_xcc = xcc_id() & 0xFu;
     __shared__ int s_stop;
     uint64_t shadow = 0;
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;
         shadow = a.shadow[slot];
+        publish_xcc(a.xcc_table, a.generation, my_xcc);
     }
     __syncthreads();
     if (s_stop) return;
+    const int v = column_on_one_xcd(a.xcc_table, a.generation, a.R, ctx, true, my_xcc, a.err,
+                                    a.timeout_ticks);
+    if (v < 0) {
+        if (threadIdx.x == 0) record_timeout(a.err, ctx, r, 0, a.generation, 0);
+        return;
+    }
+    const bool local = v == 1;
     const bool injected = r == 0 && ctx == 0;
     for (int step = 1; step <= a.nsteps; ++step) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        release_stores(local);
         const bool drop = (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && step == 1;
         if (!drop) {
             if (a.mode == SYNC_BARRIER) {
@@ -342,7 +464,7 @@ __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
             if (res.status == WAIT_TIMEOUT) record_timeout(a.err, ctx, r, step, target, res.observed);
             shadow = target;
             s_stop = res.status != WAIT_OK;
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            acquire_stores(local);
         }
         __syncthreads();
         if (s_stop) return;
@@ -401,6 +523,9 @@ DeviceState g_dev[kMaxDevices];
 struct Plan {
     int sync;
     int team;
+    int rounds;
+    int depth;
+    int cols;
     int block;
     int grid;
     int launches;
@@ -486,6 +611,8 @@ static rr_status_t check_args(void* const* bufs, int R, size_t count, int dt, in
     if (opt) {
         if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
         if (opt->team < 0 || opt->team > 4096) return RR_ERR_INVALID;
+        if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
+        if (opt->depth < 0 || opt->depth > kMaxDepth) return RR_ERR_INVALID;
         if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
             return RR_ERR_INVALID;
     }
@@ -563,20 +690,33 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
 
     const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
     p->resident_max = resident_limit(d, kernel, block);
-    const int units = R * nslices;
 
-    // team: about 16 waves per CU (two 512-thread workgroups), but each
-    // workgroup keeps at least one full unrolled pass of work per hop.
+    // Workgroups per rank (cols): about 16 waves per CU, two 512-thread
+    // workgroups.  Each interleaves `depth` lanes and runs `rounds` groups of
+    // them one after another; rounds are chosen so that one hop of the lanes in
+    // flight (3 N / rounds bytes over all ranks) stays within the Infinity Cache,
+    // so a partial is still cached when the next hop reads it.
+    const int target_cols = std::max(1, d->cus * 16 * 64 / block / R);
+    const bool fixed_depth = opt && opt->depth > 0;
+    const bool fixed_rounds = opt && opt->rounds > 0;
+    int depth = fixed_depth ? opt->depth
+                            : (requested == RR_SYNC_BARRIER ? kAutoDepthBarrier : kAutoDepthP2P);
+    int rounds;
+    if (fixed_rounds) {
+        rounds = opt->rounds;
+    } else {
+        const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
+        rounds = (int)std::max<uint64_t>(1, ceil_div(hop_bytes, kRoundBytes));
+    }
     int team;
     if (opt && opt->team > 0) {
         team = opt->team;
     } else {
-        const int target = d->cus * 16 * 64 / block;
         const uint64_t slice_vecs = p->slice_len / V;
-        const uint64_t min_vecs = (uint64_t)block * 4;
+        const uint64_t min_vecs = (uint64_t)block * 4;  // one unrolled pass per hop
         const uint64_t by_size = std::max<uint64_t>(1, slice_vecs / min_vecs);
-        team = (int)std::min<uint64_t>(by_size, (uint64_t)std::max(1, target / units));
-        team = std::max(team, 1);
+        const uint64_t wanted = ceil_div((uint64_t)target_cols * depth * rounds, nslices);
+        team = (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
     }
     // every lane needs R signals in the workspace
     const int max_team = std::max(1, kSlots / (R * nslices));
@@ -584,20 +724,48 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
         if (opt && opt->team > 0) return RR_ERR_UNSUPPORTED;
         team = max_team;
     }
+    const int lanes = nslices * team;
+    // depth * rounds must divide the lanes; automatic choices shrink to fit
+    auto fits = [&](int dd, int kk) { return dd * kk <= lanes && lanes % (dd * kk) == 0; };
+    if (!fits(depth, rounds)) {
+        if (fixed_depth && fixed_rounds) return RR_ERR_UNSUPPORTED;
+        int best_d = 1, best_k = 1;
+        for (int dd = depth; dd >= 1; --dd) {
+            if (fixed_depth && dd != depth) continue;
+            for (int kk = rounds; kk >= 1; --kk) {
+                if (fixed_rounds && kk != rounds) continue;
+                if (fits(dd, kk) && dd * kk > best_d * best_k) {
+                    best_d = dd;
+                    best_k = kk;
+                }
+            }
+        }
+        if (!fits(best_d, best_k) || (fixed_depth && best_d != depth) ||
+            (fixed_rounds && best_k != rounds))
+            return RR_ERR_UNSUPPORTED;
+        depth = best_d;
+        rounds = best_k;
+    }
     p->team = team;
+    p->depth = depth;
+    p->rounds = rounds;
+    p->cols = lanes / (depth * rounds);
     p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
-    p->grid = units * team;
-    if ((long long)units * team > (1ll << 30)) return RR_ERR_INVALID;
+    // Columns on the XCD map are padded to a multiple of 8 (idle columns exit).
+    p->xcd_map = (flags & RR_FLAG_NO_XCD_MAP) ? 0 : 1;
+    const uint64_t cols_launched = p->xcd_map ? round_up((uint64_t)p->cols, 8) : p->cols;
+    if ((uint64_t)R * cols_launched > (1ull << 30)) return RR_ERR_INVALID;
+    p->grid = (int)(R * cols_launched);
 
     const bool multi_hop = p->g_last > p->g_first;
     int sync = requested;
     if (sync == RR_SYNC_AUTO) sync = multi_hop && p->grid <= p->resident_max ? RR_SYNC_P2P : RR_SYNC_LAUNCH;
-    if ((sync == RR_SYNC_P2P || sync == RR_SYNC_BARRIER) && multi_hop && p->grid > p->resident_max)
+    if ((sync == RR_SYNC_P2P || sync == RR_SYNC_BARRIER) && multi_hop &&
+        (p->grid > p->resident_max || p->grid > kSlots))  // the XCC table has kSlots entries
         return RR_ERR_UNSUPPORTED;
     if (!multi_hop && sync != RR_SYNC_LAUNCH) sync = RR_SYNC_LAUNCH;  // one hop needs no hand-off
     p->sync = sync;
     p->launches = sync == RR_SYNC_LAUNCH ? p->g_last - p->g_first + 1 : 1;
-    p->xcd_map = !(flags & RR_FLAG_NO_XCD_MAP) && (nslices * team) % 8 == 0 ? 1 : 0;
     p->coop = sync != RR_SYNC_LAUNCH && (flags & RR_FLAG_COOPERATIVE) ? 1 : 0;
     return RR_OK;
 }
@@ -632,6 +800,9 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     }
     a.R = R;
     a.team = p.team;
+    a.cols = p.cols;
+    a.rounds = p.rounds;
+    a.depth = p.depth;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
     RingKernel k = pick_ring_kernel(dt, op, p.block);
@@ -727,6 +898,8 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
     if ((st = make_plan(d, R, count, dt, RR_SUM, nslices, phase, opt, &p)) != RR_OK) return st;
     out->sync = p.sync;
     out->team = p.team;
+    out->rounds = p.rounds;
+    out->depth = p.depth;
     out->block = p.block;
     out->grid = p.grid;
     out->launches = (R == 1 || count == 0) ? 0 : p.launches;
@@ -817,13 +990,20 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
     DeviceState* d = nullptr;
     rr_status_t st = ensure_device(&d);
     if (st != RR_OK) return st;
-    const int grid = R * ncontexts;
+    const int grid = R * (int)round_up((uint64_t)ncontexts, 8);
     if (grid > resident_limit(d, (const void*)barrier_kernel, 64)) return RR_ERR_UNSUPPORTED;
     BarrierArgs a;
     memset(&a, 0, sizeof a);
     a.sig = b->sig;
     a.shadow = b->shadow;
+    a.xcc_table = d->xcc_table;
     a.err = d->err;
+    a.nctx = ncontexts;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (++d->generation == 0) d->generation = 1;
+        a.generation = d->generation;
+    }
     a.timeout_ticks = timeout_ticks(d, opt);
     a.expected = expected_per_step;
     a.R = R;

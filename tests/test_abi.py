@@ -71,6 +71,8 @@ A = 0x7F0000000000  # 16-byte aligned addresses; never dereferenced by these tes
     dict(ptrs=[A, A + 4096], count=16, sync=9),
     dict(ptrs=[A, A + 4096], count=16, block=128),
     dict(ptrs=[A, A + 4096], count=16, team=-1),
+    dict(ptrs=[A, A + 4096], count=16, rounds=-1),
+    dict(ptrs=[A, A + 4096], count=16, depth=5),
     dict(ptrs=[A, A + 4096], count=(1 << 40) + 1),
 ])
 def test_invalid_arguments_rejected_on_host(rr, case):

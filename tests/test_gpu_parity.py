@@ -90,6 +90,35 @@ def test_multi_tile(rr, R, dtype, op, count, nslices, sync):
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"multi R={R}")
 
 
+@pytest.mark.parametrize("rounds,depth", [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2),
+                                          (1, 4), (2, 4), (1, 3)])
+@pytest.mark.parametrize("sync", ["p2p", "barrier"])
+def test_rounds_and_depth(rr, rounds, depth, sync):
+    """Lane groups run one after another and lanes interleave hop by hop inside a
+    workgroup: the same bits for every arrangement."""
+    R, count, dtype, ns = 8, (1 << 20) + 13, "fp32", 4
+    team = 8 if depth != 3 else 6
+    p = rr.plan(R, count, dtype, ns, sync=sync, team=team, rounds=rounds, depth=depth)
+    assert p["rounds"] == rounds and p["depth"] == depth
+    cols = ns * team // (rounds * depth)
+    assert p["grid"] == R * (-(-cols // 8) * 8)  # columns padded to a multiple of 8
+    log(f"case rounds={rounds} depth={depth} sync={sync} plan={p}")
+    x = workloads.generate(R, count, dtype, "uniform_pm1", 55)
+    got = run_case(rr, x, dtype, "sum", ns, sync=sync, team=team, rounds=rounds, depth=depth)
+    assert_matches_oracle(got, oracle_expect(x, "sum"), dtype, f"rounds {rounds} depth {depth}")
+
+
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("depth", [2, 4])
+def test_depth_small_ragged(rr, dtype, op, depth):
+    R, count, ns = 5, 5 * 3000 + 7, 4
+    x = workloads.generate(R, count, dtype, DIST[dtype], 66)
+    for sync in ("p2p", "barrier"):
+        log(f"case depth small {dtype} {op} depth={depth} sync={sync}")
+        got = run_case(rr, x, dtype, op, ns, sync=sync, team=2, depth=depth)
+        assert_matches_oracle(got, oracle_expect(x, op), dtype, f"depth {depth}")
+
+
 # ------------------------------------------------- the phases on their own
 
 @pytest.mark.parametrize("dtype,op", [("fp32", "sum"), ("bf16", "sum"), ("int32", "max")])
@@ -140,9 +169,10 @@ def test_invariance_across_slices_modes_teams(rr):
     ref = None
     for nslices in (1, 2, 4, 8, 16):
         for sync in ("p2p", "barrier", "launch"):
-            for team, block in ((1, 256), (4, 512), (0, 1024)):
+            for team, block, depth in ((1, 256, 1), (4, 512, 2), (0, 1024, 0)):
                 log(f"case invariance ns={nslices} sync={sync} team={team} block={block}")
-                got = run_case(rr, x, dtype, "sum", nslices, sync=sync, team=team, block=block)
+                got = run_case(rr, x, dtype, "sum", nslices, sync=sync, team=team, block=block,
+                               depth=depth)
                 if ref is None:
                     ref = got
                     assert_matches_oracle(got, oracle_expect(x, "sum"), dtype, "invariance")

@@ -155,7 +155,9 @@ def test_plan_of_the_benchmark_workload(rr):
     assert p["chunk_len"] == w.count // w.R
     assert p["hbm_bytes"] == 5 * (w.R - 1) * w.count * 4
     p = rr.plan(64, 8 * 1024 * 1024, "fp32", 8, sync="barrier")
-    assert p["sync"] == "barrier" and p["grid"] == 64 * 8 * p["team"]
+    assert p["sync"] == "barrier"
+    cols = 8 * p["team"] // (p["depth"] * p["rounds"])
+    assert p["grid"] == 64 * (-(-cols // 8) * 8)
     # too many lanes for one resident grid: auto falls back to one launch per hop
     p = rr.plan(64, 1 << 24, "fp32", 1024)
     assert p["sync"] == "launch" and p["launches"] == 126
