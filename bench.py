@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--team", type=int, default=0)
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--fused", action="store_true",
+                    help="fuse the last ReduceScatter hop with the first AllGather hop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -117,7 +119,8 @@ def main():
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
-    opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags)
+    opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags,
+                fused=args.fused)
     rr.init()
     p = rr.plan(w.R, w.count, w.dtype, w.nslices, **opts)
     log(f"workload {w.name}: R={w.R} {w.dtype} {w.op} {w.bytes_per_rank / 2**20:.1f} MiB/rank "
@@ -234,6 +237,7 @@ def main():
         "config": {"workload": w.name, "R": w.R, "bytes_per_rank": w.bytes_per_rank,
                    "op": w.op, "nslices": w.nslices, "sync": p["sync"], "team": p["team"],
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
+                   "fused_boundary": bool(p["fused"]),
                    "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
     }

@@ -112,6 +112,11 @@ typedef enum {
 #define RR_FLAG_NO_XCD_MAP       0x1u /* plain block -> (rank, lane) order; hand-offs then
                                          cross XCDs and write L2 back every hop */
 #define RR_FLAG_NO_POINTER_CHECK 0x2u /* skip the per-call allocation-extent check */
+#define RR_FLAG_FUSED_BOUNDARY   0x8u /* AllReduce only: the last ReduceScatter hop also
+                                         stores the finished chunk in the owner's
+                                         successor (the ring post's recvReduceCopySend,
+                                         sections 8-9), so the first AllGather hop moves
+                                         no data: 5(R-1)N - N bytes instead of 5(R-1)N */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -145,6 +150,8 @@ typedef struct {
     int32_t resident_max;/* workgroups the device can hold at once for this kernel */
     int32_t rounds;      /* lane groups each workgroup runs one after another */
     int32_t depth;       /* lanes each workgroup interleaves */
+    int32_t fused;       /* 1 if the boundary hop is fused (RR_FLAG_FUSED_BOUNDARY) */
+    int32_t reserved;
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */
     uint64_t sub_len;    /* elements per team member */

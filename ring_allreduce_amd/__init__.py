@@ -45,6 +45,7 @@ INJECT_DROP_ARRIVAL = 0x2
 FLAG_NO_XCD_MAP = 0x1
 FLAG_NO_POINTER_CHECK = 0x2
 FLAG_COOPERATIVE = 0x4
+FLAG_FUSED_BOUNDARY = 0x8
 
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16"}
 ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
@@ -62,7 +63,8 @@ class _Plan(ctypes.Structure):
                 ("grid", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("xcd_map", ctypes.c_int32), ("cooperative", ctypes.c_int32),
                 ("resident_max", ctypes.c_int32), ("rounds", ctypes.c_int32),
-                ("depth", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
+                ("depth", ctypes.c_int32), ("fused", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
                 ("slice_len", ctypes.c_uint64), ("sub_len", ctypes.c_uint64),
                 ("hbm_bytes", ctypes.c_uint64)]
 
@@ -155,7 +157,10 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
-def _options(sync="auto", team=0, block=0, rounds=0, timeout_ns=0, inject=0, flags=0, depth=0):
+def _options(sync="auto", team=0, block=0, rounds=0, timeout_ns=0, inject=0, flags=0, depth=0,
+             fused=False):
+    if fused:
+        flags |= FLAG_FUSED_BOUNDARY
     return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, rounds,
                    timeout_ns, inject, flags, depth, 0)
 

@@ -67,7 +67,7 @@ struct RingArgs {
     ErrorRecord* err;
     uint64_t timeout_ticks;
     uint32_t generation; // per-launch tag, never 0
-    int32_t pad0;
+    int32_t fuse;        // 1: fused boundary (the last ReduceScatter hop also does the first AllGather hop)
     int32_t R;
     int32_t team;
     int32_t g_first;     // hops run by this launch, 1-based, inclusive
@@ -205,7 +205,7 @@ __device__ __forceinline__ u32x4 load_in(__amdgpu_buffer_rsrc_t rs, uint32_t vec
 // U vectors per thread in flight, then a scalar tail (only at the ragged end).
 template <int DT, int OP, int BLOCK, int U>
 __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void* dstbuf,
-                                          uint64_t lo, uint64_t hi) {
+                                          void* dst2buf, uint64_t lo, uint64_t hi) {
     constexpr int ES = ElemBytes<DT>::value;
     constexpr int V = 16 / ES;
     const uint64_t n = hi - lo;
@@ -213,8 +213,30 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
     const char* sb = (const char*)srcbuf + lo * ES;
     const __amdgpu_buffer_rsrc_t rs = incoming(sb, n * ES);
     u32x4* __restrict__ d = (u32x4*)((char*)dstbuf + lo * ES);
+    u32x4* d2 = dst2buf ? (u32x4*)((char*)dst2buf + lo * ES) : nullptr;
     uint32_t i = threadIdx.x;
-    if (reduce) {
+    if (reduce && d2) {
+        // recvReduceCopySend: the finished chunk goes to the owner's buffer and on
+        // to the owner's successor in the same pass
+        for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
+            u32x4 x[U], y[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
+#pragma unroll
+            for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 v = fold4<DT, OP>(x[u], y[u]);
+                d[i + u * BLOCK] = v;
+                d2[i + u * BLOCK] = v;
+            }
+        }
+        for (; i < nv; i += BLOCK) {
+            const u32x4 v = fold4<DT, OP>(load_in(rs, i), d[i]);
+            d[i] = v;
+            d2[i] = v;
+        }
+    } else if (reduce) {
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
@@ -240,29 +262,29 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
     if (t < n) {
         char* dp = (char*)dstbuf + (lo + t) * ES;
         const int off = (int)(t * ES);
+        char* dp2 = dst2buf ? (char*)dst2buf + (lo + t) * ES : nullptr;
         if constexpr (ES == 2) {
             const uint16_t in =
                 __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kAuxDeviceScope);
-            if (reduce)
-                *(uint16_t*)dp = (uint16_t)Fold<DT, OP>::half(in, *(const uint16_t*)dp);
-            else
-                *(uint16_t*)dp = in;
+            const uint16_t v =
+                reduce ? (uint16_t)Fold<DT, OP>::half(in, *(const uint16_t*)dp) : in;
+            *(uint16_t*)dp = v;
+            if (dp2) *(uint16_t*)dp2 = v;
         } else {
             const uint32_t in = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kAuxDeviceScope);
-            if (reduce)
-                *(uint32_t*)dp = Fold<DT, OP>::lane(in, *(const uint32_t*)dp);
-            else
-                *(uint32_t*)dp = in;
+            const uint32_t v = reduce ? Fold<DT, OP>::lane(in, *(const uint32_t*)dp) : in;
+            *(uint32_t*)dp = v;
+            if (dp2) *(uint32_t*)dp2 = v;
         }
     }
 }
 
 template <int DT, int OP, int BLOCK, int U>
 __device__ __forceinline__ void hop_body(bool reduce, const void* srcbuf, void* dstbuf,
-                                         uint64_t lo, uint64_t hi) {
+                                         void* dst2buf, uint64_t lo, uint64_t hi) {
     constexpr uint64_t kPiece = kPieceBytes / ElemBytes<DT>::value;  // elements, vector multiple
     for (uint64_t p = lo; p < hi; p += kPiece)
-        hop_piece<DT, OP, BLOCK, U>(reduce, srcbuf, dstbuf, p, umin(p + kPiece, hi));
+        hop_piece<DT, OP, BLOCK, U>(reduce, srcbuf, dstbuf, dst2buf, p, umin(p + kPiece, hi));
 }
 
 template <int DT, int OP, int BLOCK>
@@ -273,6 +295,7 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
     const int r = pl.rank, col = pl.col;
     if (col >= a.cols) return;  // padding column
     const int succ = r + 1 == R ? 0 : r + 1;
+    const int succ2 = succ + 1 == R ? 0 : succ + 1;
     const bool synced = a.g_last > a.g_first;
 
     __shared__ int s_stop;
@@ -350,10 +373,16 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
                     c = wrap(r + 2 - (g - (R - 1)), R);
                     reduce = false;
                 }
+                // Fused boundary: the last ReduceScatter hop also stores the finished
+                // chunk in the owner's successor, so the first AllGather hop only
+                // passes the hand-off on.
+                void* dst2 = a.fuse && g == R - 1 ? a.bufs[succ2] : nullptr;
+                const bool skip = a.fuse && g == R;
                 const uint64_t base = (uint64_t)c * a.chunk_len;
                 const uint64_t lo = base + off_lo[p];
                 const uint64_t hi = umin(base + off_hi[p], a.count);
-                if (lo < hi) hop_body<DT, OP, BLOCK, U>(reduce, a.bufs[r], a.bufs[succ], lo, hi);
+                if (lo < hi && !skip)
+                    hop_body<DT, OP, BLOCK, U>(reduce, a.bufs[r], a.bufs[succ], dst2, lo, hi);
 
                 if (g < a.g_last) {
                     if (!decided) {
@@ -521,6 +550,7 @@ std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
 struct Plan {
+    int fuse;
     int sync;
     int team;
     int rounds;
@@ -686,7 +716,10 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     const uint64_t nbytes = (uint64_t)count * elem_bytes(dt);
     const uint64_t rs = phase != 2 ? 3ull * (uint64_t)(R - 1) * nbytes : 0;
     const uint64_t ag = phase != 1 ? 2ull * (uint64_t)(R - 1) * nbytes : 0;
-    p->hbm_bytes = R > 1 ? rs + ag : 0;
+    // fusion applies to a whole AllReduce only; it saves the first AllGather
+    // hop's load: one chunk per rank, N bytes in all
+    p->fuse = phase == 0 && R > 1 && (flags & RR_FLAG_FUSED_BOUNDARY) ? 1 : 0;
+    p->hbm_bytes = R > 1 ? rs + ag - (p->fuse ? nbytes : 0) : 0;
 
     const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
     p->resident_max = resident_limit(d, kernel, block);
@@ -803,6 +836,7 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.cols = p.cols;
     a.rounds = p.rounds;
     a.depth = p.depth;
+    a.fuse = p.fuse;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
     RingKernel k = pick_ring_kernel(dt, op, p.block);
@@ -900,6 +934,7 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
     out->team = p.team;
     out->rounds = p.rounds;
     out->depth = p.depth;
+    out->fused = p.fuse;
     out->block = p.block;
     out->grid = p.grid;
     out->launches = (R == 1 || count == 0) ? 0 : p.launches;

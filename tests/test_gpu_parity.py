@@ -119,6 +119,53 @@ def test_depth_small_ragged(rr, dtype, op, depth):
         assert_matches_oracle(got, oracle_expect(x, op), dtype, f"depth {depth}")
 
 
+# ------------------------------- fused boundary (recvReduceCopySend step)
+
+FUSED_SMALL = [(2, 37, 1, 1), (3, 1000, 2, 1), (5, 12345, 4, 3), (8, 8 * 1024 + 5, 4, 2),
+               (16, 16 * 8 * 33 + 7, 5, 1), (7, 6, 1, 1)]
+
+
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("fp32", "max"),
+                                      ("bf16", "sum"), ("bf16", "max")])
+@pytest.mark.parametrize("R,count,nslices,team", FUSED_SMALL)
+@pytest.mark.parametrize("sync", ["p2p", "barrier", "launch"])
+def test_fused_boundary_small(rr, dtype, op, R, count, nslices, team, sync):
+    """The last ReduceScatter hop stores the finished chunk twice and the first
+    AllGather hop moves nothing: the same bits as the plain ring."""
+    log(f"case fused {dtype} {op} R={R} count={count} ns={nslices} team={team} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], R * 17 + count % 89)
+    got = run_case(rr, x, dtype, op, nslices, sync=sync, team=team, fused=True)
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"fused R={R} count={count}")
+
+
+@pytest.mark.parametrize("rounds,depth,sync", [(1, 1, "p2p"), (2, 2, "p2p"), (1, 4, "barrier"),
+                                               (4, 1, "barrier"), (0, 0, "auto")])
+def test_fused_boundary_multi_tile(rr, rounds, depth, sync):
+    R, count, dtype, ns = 8, (1 << 20) + 13, "fp32", 4
+    p = rr.plan(R, count, dtype, ns, sync=sync, rounds=rounds, depth=depth, fused=True)
+    plain = rr.plan(R, count, dtype, ns, sync=sync, rounds=rounds, depth=depth)
+    assert p["fused"] == 1 and plain["fused"] == 0
+    assert p["hbm_bytes"] == plain["hbm_bytes"] - count * 4
+    log(f"case fused multi rounds={rounds} depth={depth} sync={sync} plan={p}")
+    x = workloads.generate(R, count, dtype, "uniform_pm1", 57)
+    got = run_case(rr, x, dtype, "sum", ns, sync=sync, rounds=rounds, depth=depth, fused=True)
+    assert_matches_oracle(got, oracle_expect(x, "sum"), dtype, "fused multi")
+
+
+def test_fused_boundary_r64_and_phases(rr):
+    R, count = 64, 64 * 4096 + 5
+    x = workloads.generate(R, count, "bf16", "normal", 58)
+    for sync in ("barrier", "p2p"):
+        log(f"case fused R=64 sync={sync}")
+        got = run_case(rr, x, "bf16", "sum", 8, sync=sync, fused=True)
+        assert_matches_oracle(got, oracle_expect(x, "sum"), "bf16", f"fused R=64 {sync}")
+    # the flag has no effect on a lone phase
+    assert rr.plan(8, 1 << 16, "fp32", 2, phase="reduce_scatter", fused=True)["fused"] == 0
+    x = workloads.generate(5, 5 * 999 + 1, "fp32", "uniform_pm1", 59)
+    got = run_case(rr, x, "fp32", "sum", 2, phase="reduce_scatter", fused=True)
+    assert_matches_oracle(got, oracle_expect(x, "sum", "reduce_scatter"), "fp32", "fused RS")
+
+
 # ------------------------------------------------- the phases on their own
 
 @pytest.mark.parametrize("dtype,op", [("fp32", "sum"), ("bf16", "sum"), ("int32", "max")])
@@ -329,6 +376,12 @@ def test_full_r8_bf16_256MiB(rr):
 
 def test_full_r64_fp32_32MiB(rr):
     _full_size(rr, workloads.R64_FP32_32MIB, 3000)
+
+
+@pytest.mark.parametrize("w", [workloads.R8_FP32_64MIB, workloads.R64_FP32_32MIB],
+                         ids=lambda w: w.name)
+def test_full_fused_boundary(rr, w):
+    _full_size(rr, w, 5000, dict(fused=True))
 
 
 @pytest.mark.parametrize("k", range(0, 9))
