@@ -246,11 +246,16 @@ def main():
 
 
 def barrier_latency(rr, torch):
-    """Per-step latency of the counting barrier on its own: one 64-lane workgroup per
-    (context, waiter); per step each waiter arrives (adds 1 to the other R-1
-    waiters' signals, or to its successor's in p2p mode) and waits for its own
-    signal to advance by the expected count.  us/step = (t(nsteps) - t(0)) / nsteps,
-    best of 5 timed launches each."""
+    """Per-step latency of the barrier on its own, in three layouts: one 64-lane
+    workgroup per (context, waiter); per step each waiter arrives and waits.
+      barrier   counting signal: adds 1 to each other waiter's one signal, waits
+                for its own to advance by R-1
+      per_peer  per-peer slots: adds 1 to its own slot in each other waiter's
+                row, waits for each of the R-1 slots of its row to advance by 1
+      p2p       adds 1 to its successor's signal, waits for 1
+    us/step = (t(nsteps) - t(0)) / nsteps, best of 5 timed launches each.  Then,
+    for the counting barrier, audited runs count the steps a waiter passed on a
+    stand-in arrival from a peer one step ahead (a lower bound)."""
     rr.init()
     b = rr.CountingBarrier(64, 8)
     stream = torch.cuda.current_stream()
@@ -270,17 +275,29 @@ def barrier_latency(rr, torch):
         return best
 
     steps = 2000
-    for mode in ("barrier", "p2p"):
+    for mode in ("barrier", "per_peer", "p2p"):
         for nctx in (1, 8):
             for R in (2, 4, 8, 16, 32, 64):
                 b.run(R, 100, nctx, mode=mode)  # warm
                 t0 = timed(R, 0, nctx, mode)
                 t1 = timed(R, steps, nctx, mode)
                 us = (t1 - t0) * 1e3 / steps
-                print(json.dumps({"metric": "counting barrier latency per step", "mode": mode,
+                per_waiter = 1 if mode == "p2p" else R - 1
+                print(json.dumps({"metric": "barrier latency per step", "mode": mode,
                                   "R": R, "contexts": nctx, "us_per_step": round(us, 3),
-                                  "atomics_per_step": nctx * R * ((R - 1) if mode == "barrier" else 1),
+                                  "atomics_per_step": nctx * R * per_waiter,
+                                  "slots_per_waiter": 1 if mode != "per_peer" else R - 1,
                                   "empty_launch_ms": round(t0, 4)}), flush=True)
+    for R in (4, 8, 16, 64):
+        nctx, asteps = 8, 500
+        b.reset()
+        b.run(R, asteps, nctx, mode="barrier", flags=rr.FLAG_AUDIT)
+        torch.cuda.synchronize()
+        rr.check_kernel_error()
+        early = sum(b.early_passes(c, q) for c in range(nctx) for q in range(R))
+        print(json.dumps({"metric": "counting barrier early passes (audited)", "R": R,
+                          "contexts": nctx, "steps": asteps, "waits": nctx * R * asteps,
+                          "early_passes": early}), flush=True)
     b.close()
     return 0
 

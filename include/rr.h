@@ -99,7 +99,11 @@ typedef enum {
     RR_SYNC_BARRIER = 2, /* persistent kernel; every hop ends with a counting barrier
                             over all R ranks of the lane: each workgroup adds 1 to
                             every other rank's signal, a waiter expects R-1 */
-    RR_SYNC_LAUNCH = 3   /* one kernel launch per hop; stream order is the barrier */
+    RR_SYNC_LAUNCH = 3,  /* one kernel launch per hop; stream order is the barrier */
+    RR_SYNC_PER_PEER = 4 /* counting_barrier_run only: one slot per (waiter, peer);
+                            each peer adds 1 to its own slot and a waiter waits for
+                            every slot (the layout the DeepEP pull request replaced,
+                            section "Fix"); the ring calls reject it */
 } rr_sync_t;
 
 /* Fault injection, for failure tests only.  Each makes one waiter's wait
@@ -107,6 +111,16 @@ typedef enum {
 #define RR_INJECT_EXTRA_EXPECTED 0x1u /* rank 0, context 0 expects one arrival too many
                                          at its first wait */
 #define RR_INJECT_DROP_ARRIVAL   0x2u /* rank 0, context 0 skips its first arrival */
+#define RR_INJECT_DEFER_ARRIVAL  0x4u /* counting_barrier_run, barrier modes: waiter 0 of
+                                         context 0 holds back its step-1 and step-2
+                                         arrivals at waiter 1 until it has passed
+                                         step 2, which needs waiter 1 past step 1.
+                                         A per-peer barrier (and R = 2) therefore
+                                         times out naming the peer, while a counting
+                                         barrier with R >= 3 passes on a stand-in
+                                         from another peer one step ahead (DeepEP
+                                         pull request, section "Scoped to the rail
+                                         team") and completes */
 
 /* Flags. */
 #define RR_FLAG_NO_XCD_MAP       0x1u /* plain block -> (rank, lane) order; hand-offs then
@@ -117,6 +131,13 @@ typedef enum {
                                          successor (the ring post's recvReduceCopySend,
                                          sections 8-9), so the first AllGather hop moves
                                          no data: 5(R-1)N - N bytes instead of 5(R-1)N */
+#define RR_FLAG_AUDIT            0x10u /* counting_barrier_run, RR_SYNC_BARRIER: every
+                                         arrival also bumps the sender's per-peer slot
+                                         (a witness, released before the counting add);
+                                         after each step a waiter counts it as an early
+                                         pass if some peer's witness has not advanced.
+                                         A lower bound (a witness may land just before
+                                         its counting add); slower, for tests only */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -160,12 +181,15 @@ typedef struct {
 
 /* Device-side failure record (rr_last_kernel_error).  Following the DeepEP
    pull request (section "Fix"), a counting signal cannot name the missing peer,
-   so the record gives the signal and how many arrivals were missing. */
+   so the record gives the signal and how many arrivals were missing; only a
+   per-peer barrier (RR_SYNC_PER_PEER) can name the peer. */
 typedef struct {
     int32_t status;    /* RR_OK or RR_ERR_TIMEOUT */
     int32_t ctx;       /* context (lane = slice * team + member) of the waiter */
     int32_t waiter;    /* its virtual rank */
     int32_t hop;       /* hop (or barrier step) it was about to start */
+    int32_t peer;      /* the peer that did not arrive (per-peer slots), else -1 */
+    int32_t reserved;
     uint64_t expected; /* signal value it waited for */
     uint64_t observed; /* last value it read; expected - observed are missing */
 } rr_error_record_t;
@@ -216,8 +240,10 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
 
 /* A standalone set of counting signals: `ncontexts` contexts of `nwaiters`
    waiters, one 64-bit signal and one shadow each (DeepEP pull request, section
-   "Fix": one signal per waiter whatever the team size).  Caller-owned; lives in
-   device memory of the current device. */
+   "Fix": one signal per waiter whatever the team size), plus, for comparison,
+   the per-peer layout that pull request replaced: a row of nwaiters slots and
+   shadows per waiter.  Caller-owned; lives in device memory of the current
+   device: about ncontexts * nwaiters * (144 + 16 * round_up(nwaiters, 16)) bytes. */
 typedef struct rr_counting_barrier rr_counting_barrier_t;
 
 /* Errors: RR_ERR_INVALID (nwaiters outside 1..64, ncontexts outside 1..1024,
@@ -239,14 +265,30 @@ rr_status_t counting_barrier_preset(rr_counting_barrier_t *b, uint64_t value, rr
 rr_status_t counting_barrier_read(rr_counting_barrier_t *b, int ctx, int waiter, uint64_t *value,
                                   uint64_t *shadow);
 
+/* Reads the per-peer slot of `peer` in `waiter`'s row and the waiter's shadow
+   of it, synchronously.  Errors: RR_ERR_INVALID (indices out of range or
+   peer == waiter), RR_ERR_HIP. */
+rr_status_t counting_barrier_read_peer(rr_counting_barrier_t *b, int ctx, int waiter, int peer,
+                                       uint64_t *value, uint64_t *shadow);
+
+/* Steps that `waiter` passed, in audited counting runs (RR_FLAG_AUDIT) since
+   the last reset, before every peer's arrival for that step had reached it: a
+   stand-in from a peer one step ahead completed its count.  Synchronous.
+   Errors: RR_ERR_INVALID, RR_ERR_HIP. */
+rr_status_t counting_barrier_early_passes(rr_counting_barrier_t *b, int ctx, int waiter,
+                                          uint64_t *count);
+
 /* Runs `nsteps` barrier steps over the first `ncontexts` contexts with R
    waiters each, one workgroup per (context, waiter), in one kernel.  Per step a
    waiter arrives (opt->sync RR_SYNC_BARRIER or AUTO: adds 1 to every other
-   waiter's signal in its context; RR_SYNC_P2P: adds 1 to its successor's) and
-   then advances its shadow by `expected_per_step` and waits for its own signal.
-   The right expectation is R-1 (barrier) or 1 (p2p); a larger one times out
-   (RR_ERR_TIMEOUT from rr_last_kernel_error, with the missing count).  With
-   nsteps == 0 it launches the same kernel doing nothing, to time the launch.
+   waiter's signal in its context; RR_SYNC_P2P: adds 1 to its successor's;
+   RR_SYNC_PER_PEER: adds 1 to its own slot in every other waiter's row) and
+   then advances its shadow by `expected_per_step` and waits for its own signal
+   (per peer: advances every slot's shadow by it and waits for every slot).
+   The right expectation is R-1 (barrier) or 1 (p2p, per peer); a larger one
+   times out (RR_ERR_TIMEOUT from rr_last_kernel_error, with the missing count;
+   per peer also with the missing peer).  With nsteps == 0 it launches the same
+   kernel doing nothing, to time the launch.
    Errors: RR_ERR_INVALID (R > nwaiters, ncontexts > the object's, nsteps < 0),
    RR_ERR_UNSUPPORTED (grid cannot be resident), RR_ERR_HIP. */
 rr_status_t counting_barrier_run(rr_counting_barrier_t *b, int R, int nsteps, int ncontexts,

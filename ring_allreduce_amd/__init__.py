@@ -32,7 +32,7 @@ RR_MAX_SLICES = 1024
 
 DTYPES = {"int32": 0, "fp32": 1, "bf16": 2}
 OPS = {"sum": 0, "max": 1}
-SYNCS = {"auto": 0, "p2p": 1, "barrier": 2, "launch": 3}
+SYNCS = {"auto": 0, "p2p": 1, "barrier": 2, "launch": 3, "per_peer": 4}
 SYNC_NAMES = {v: k for k, v in SYNCS.items()}
 PHASES = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 
@@ -42,10 +42,12 @@ RR_OK, RR_ERR_INVALID, RR_ERR_UNSUPPORTED, RR_ERR_HIP, RR_ERR_TIMEOUT, RR_ERR_NO
 
 INJECT_EXTRA_EXPECTED = 0x1
 INJECT_DROP_ARRIVAL = 0x2
+INJECT_DEFER_ARRIVAL = 0x4
 FLAG_NO_XCD_MAP = 0x1
 FLAG_NO_POINTER_CHECK = 0x2
 FLAG_COOPERATIVE = 0x4
 FLAG_FUSED_BOUNDARY = 0x8
+FLAG_AUDIT = 0x10
 
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16"}
 ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
@@ -71,7 +73,8 @@ class _Plan(ctypes.Structure):
 
 class ErrorRecord(ctypes.Structure):
     _fields_ = [("status", ctypes.c_int32), ("ctx", ctypes.c_int32), ("waiter", ctypes.c_int32),
-                ("hop", ctypes.c_int32), ("expected", ctypes.c_uint64),
+                ("hop", ctypes.c_int32), ("peer", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("expected", ctypes.c_uint64),
                 ("observed", ctypes.c_uint64)]
 
     def as_dict(self):
@@ -105,6 +108,9 @@ _cb_destroy = _sig("counting_barrier_destroy", _i, _vp)
 _cb_reset = _sig("counting_barrier_reset", _i, _vp, _vp)
 _cb_preset = _sig("counting_barrier_preset", _i, _vp, _u64, _vp)
 _cb_read = _sig("counting_barrier_read", _i, _vp, _i, _i, ctypes.POINTER(_u64), ctypes.POINTER(_u64))
+_cb_read_peer = _sig("counting_barrier_read_peer", _i, _vp, _i, _i, _i, ctypes.POINTER(_u64),
+                     ctypes.POINTER(_u64))
+_cb_early = _sig("counting_barrier_early_passes", _i, _vp, _i, _i, ctypes.POINTER(_u64))
 _cb_run = _sig("counting_barrier_run", _i, _vp, _i, _i, _i, _u64, _OPT, _vp)
 _last_kernel_error = _sig("rr_last_kernel_error", _i, _vp, ctypes.POINTER(ErrorRecord))
 _init = _sig("rr_init", _i)
@@ -118,7 +124,8 @@ _finalize = _sig("rr_finalize", None)
 EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
             "reduce_scatter_ring_ex", "all_gather_ring_ex", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
-            "counting_barrier_preset", "counting_barrier_read", "counting_barrier_run",
+            "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
+            "counting_barrier_early_passes", "counting_barrier_run",
             "rr_last_kernel_error", "rr_init", "rr_workspace_preset", "rr_hbm_copy",
             "rr_status_string", "rr_abi_version", "rr_finalize"]
 
@@ -298,7 +305,7 @@ class CountingBarrier:
     def run(self, R: int, nsteps: int, ncontexts: int = 1, expected: int | None = None,
             mode: str = "barrier", stream=None, **opts) -> None:
         if expected is None:
-            expected = R - 1 if mode == "barrier" else 1
+            expected = R - 1 if mode == "barrier" else 1  # p2p and per_peer: 1 per slot
         o = _options(sync=mode, **opts)
         _check(_cb_run(self._h, R, nsteps, ncontexts, expected, ctypes.byref(o),
                        _stream_handle(stream)), "counting_barrier_run")
@@ -308,6 +315,18 @@ class CountingBarrier:
         _check(_cb_read(self._h, ctx, waiter, ctypes.byref(v), ctypes.byref(s)),
                "counting_barrier_read")
         return v.value, s.value
+
+    def read_peer(self, ctx: int, waiter: int, peer: int):
+        """(slot value, shadow) of ``peer``'s per-peer slot in ``waiter``'s row."""
+        v, s = _u64(), _u64()
+        _check(_cb_read_peer(self._h, ctx, waiter, peer, ctypes.byref(v), ctypes.byref(s)),
+               "counting_barrier_read_peer")
+        return v.value, s.value
+
+    def early_passes(self, ctx: int, waiter: int) -> int:
+        n = _u64()
+        _check(_cb_early(self._h, ctx, waiter, ctypes.byref(n)), "counting_barrier_early_passes")
+        return n.value
 
     def reset(self, stream=None) -> None:
         _check(_cb_reset(self._h, _stream_handle(stream)), "counting_barrier_reset")

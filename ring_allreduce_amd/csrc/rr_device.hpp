@@ -22,7 +22,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
 enum : int { OP_SUM = 0, OP_MAX = 1 };
-enum : int { SYNC_NONE = 0, SYNC_P2P = 1, SYNC_BARRIER = 2 };
+enum : int { SYNC_NONE = 0, SYNC_P2P = 1, SYNC_BARRIER = 2, SYNC_PER_PEER = 3 };
 
 template <int DT> struct ElemBytes { static constexpr int value = DT == DT_BF16 ? 2 : 4; };
 
@@ -121,6 +121,8 @@ struct ErrorRecord {
     int32_t ctx;
     int32_t waiter;
     int32_t hop;
+    int32_t peer;       // the peer whose arrival is missing; -1 for a counting signal
+    int32_t pad;
     uint64_t expected;
     uint64_t observed;
 };
@@ -168,7 +170,7 @@ __device__ __forceinline__ WaitResult sig_wait(const uint64_t* sig, uint64_t tar
 
 // First give-up on the device wins the record; later ones only stop.
 __device__ __noinline__ void record_timeout(ErrorRecord* err, int ctx, int waiter, int hop,
-                                            uint64_t expected, uint64_t observed) {
+                                            uint64_t expected, uint64_t observed, int peer = -1) {
     uint64_t clear = 0;
     if (__hip_atomic_compare_exchange_strong(&err->flag, &clear, (uint64_t)1, __ATOMIC_RELAXED,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -176,6 +178,7 @@ __device__ __noinline__ void record_timeout(ErrorRecord* err, int ctx, int waite
         err->ctx = ctx;
         err->waiter = waiter;
         err->hop = hop;
+        err->peer = peer;
         err->expected = expected;
         err->observed = observed;
     }

@@ -428,26 +428,81 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
 // ---------------------------------------------------------- barrier only --
 
 struct BarrierArgs {
-    uint64_t* sig;
+    uint64_t* sig;       // counting signals, one per (context, waiter)
     uint64_t* shadow;
+    uint64_t* pp_sig;    // per-peer slots: a row of pp_row words per (context, waiter)
+    uint64_t* pp_shadow;
+    uint64_t* early;     // per (context, waiter): steps passed before every peer arrived
     uint64_t* xcc_table;
     ErrorRecord* err;
     uint64_t timeout_ticks;
-    uint64_t expected;  // arrivals per step
-    int32_t R;          // waiters per context taking part
-    int32_t stride;     // waiters per context in the object's layout
+    uint64_t expected;   // arrivals per step (counting) or per slot and step (per peer)
+    int32_t R;           // waiters per context taking part
+    int32_t stride;      // waiters per context in the object's layout
+    int32_t pp_row;      // words per per-peer row
     int32_t nsteps;
-    int32_t mode;       // SYNC_P2P or SYNC_BARRIER
-    int32_t nctx;       // contexts taking part (columns; the grid is padded to 8)
+    int32_t mode;        // SYNC_P2P, SYNC_BARRIER or SYNC_PER_PEER
+    int32_t nctx;        // contexts taking part (columns; the grid is padded to 8)
     uint32_t generation;
     uint32_t inject;
+    int32_t audit;       // counting mode: also keep per-peer witnesses and count early passes
     int32_t pad;
 };
 
-// One 64-lane workgroup per (context, waiter), laid out like the ring kernel's
-// columns so a context's waiters share an XCD.  Each step: release, arrive,
-// advance the shadow by `expected`, wait, acquire -- the same hand-off the ring
-// kernel performs between hops, without the payload.
+struct PeerWait {
+    int status;
+    int lane;  // first unsatisfied lane on a timeout
+    uint64_t expected, observed;
+};
+
+// Per-peer wait, for the whole wave: each active lane watches one slot until it
+// reaches that lane's target; the wave leaves when every lane is satisfied.
+// Every decision that ends the loop is wave-uniform.
+__device__ PeerWait peer_wait(const uint64_t* slot, bool active, uint64_t target,
+                              const ErrorRecord* err, uint64_t timeout_ticks) {
+    uint64_t v = active ? sig_read(slot) : target;
+    bool ok = !active || rolling_le(target, v);
+    if (__all(ok)) return {WAIT_OK, -1, 0, 0};
+    const uint64_t start = wall_clock64();
+    uint32_t spins = 0;
+    for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        if (!ok) {
+            v = sig_read(slot);
+            ok = rolling_le(target, v);
+        }
+        if (__all(ok)) return {WAIT_OK, -1, 0, 0};
+        if ((++spins & 31u) == 0u) {
+            const uint32_t stop =
+                __builtin_amdgcn_readfirstlane((uint32_t)(sig_read(&err->flag) != 0));
+            if (stop) return {WAIT_ABORT, -1, 0, 0};
+            if (wall_clock64() - start > timeout_ticks) {
+                const uint64_t bad = __ballot(!ok);
+                const int lane = (int)__builtin_ctzll(bad);
+                const uint64_t e = ((uint64_t)(uint32_t)__shfl((int)(target >> 32), lane) << 32) |
+                                   (uint32_t)__shfl((int)(uint32_t)target, lane);
+                const uint64_t o = ((uint64_t)(uint32_t)__shfl((int)(v >> 32), lane) << 32) |
+                                   (uint32_t)__shfl((int)(uint32_t)v, lane);
+                return {WAIT_TIMEOUT, lane, e, o};
+            }
+        }
+    }
+}
+
+// One 64-lane workgroup (one wave) per (context, waiter), laid out like the ring
+// kernel's columns so a context's waiters share an XCD.  Each step: release,
+// arrive, advance the shadow, wait, acquire -- the same hand-off the ring kernel
+// performs between hops, without the payload.  Lane i < R-1 serves the peer
+// q = r+1+i (mod R): it arrives at q, and in per-peer mode it also watches
+// q's slot in this waiter's row.
+//
+// Arrivals per step:
+//   P2P       one add to the successor's counting signal
+//   BARRIER   one add to each other waiter's counting signal; the waiter
+//             expects R-1 on its own (the DeepEP pull request's counting barrier)
+//   PER_PEER  one add to this waiter's slot in each other waiter's row; the
+//             waiter expects every slot of its row to advance (the per-peer
+//             layout the pull request replaced)
 __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
     const Place pl = place_of(blockIdx.x, a.R, true);
     const int r = pl.rank, ctx = pl.col;
@@ -471,34 +526,92 @@ __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
     }
     const bool local = v == 1;
     const bool injected = r == 0 && ctx == 0;
+    const int lane = (int)threadIdx.x;
+    const bool peer_lane = lane < a.R - 1;
+    const int q = wrap(r + 1 + lane, a.R);
+    const bool per_peer = a.mode == SYNC_PER_PEER;
+    const bool audit = a.audit && a.mode == SYNC_BARRIER;
+    const bool use_pp = per_peer || audit;
+    // my slot in q's row (where I arrive) and q's slot in my row (what I watch)
+    uint64_t* const out_pp = a.pp_sig + (uint64_t)(ctx * a.stride + q) * a.pp_row + r;
+    uint64_t* const in_pp = a.pp_sig + (uint64_t)slot * a.pp_row + q;
+    uint64_t* const in_pp_shadow = a.pp_shadow + (uint64_t)slot * a.pp_row + q;
+    uint64_t pp_shadow = use_pp && peer_lane ? *in_pp_shadow : 0;
+    uint64_t early = 0;
+    // RR_INJECT_DEFER_ARRIVAL: waiter 0 of context 0 holds back its step-1 and
+    // step-2 arrivals at waiter 1 until it has passed step 2 (with one step,
+    // until the end).  Its step-2 arrival must be held too: otherwise it stands
+    // in for its own late step-1 arrival, which both layouts allow.
+    const bool defer = (a.inject & RR_INJECT_DEFER_ARRIVAL) && injected && peer_lane && q == 1;
+
+    auto arrive = [&]() {
+        if (per_peer) {
+            sig_add(out_pp, 1);
+            return;
+        }
+        if (audit) {
+            // the witness is visible before the counting arrival it stands for
+            sig_add(out_pp, 1);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        }
+        sig_add(&a.sig[(uint64_t)(ctx * a.stride + q) * kSignalStride], 1);
+    };
+
     for (int step = 1; step <= a.nsteps; ++step) {
         release_stores(local);
         const bool drop = (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && step == 1;
         if (!drop) {
-            if (a.mode == SYNC_BARRIER) {
-                if ((int)threadIdx.x < a.R - 1) {
-                    const int q = wrap(r + 1 + (int)threadIdx.x, a.R);
-                    sig_add(&a.sig[(uint64_t)(ctx * a.stride + q) * kSignalStride], 1);
-                }
-            } else if (threadIdx.x == 0) {
-                const int q = r + 1 == a.R ? 0 : r + 1;
-                sig_add(&a.sig[(uint64_t)(ctx * a.stride + q) * kSignalStride], 1);
+            if (a.mode == SYNC_P2P) {
+                if (lane == 0) sig_add(&a.sig[(uint64_t)(ctx * a.stride + q) * kSignalStride], 1);
+            } else if (peer_lane && !(defer && step <= 2)) {
+                arrive();
             }
         }
-        if (threadIdx.x == 0) {
-            uint64_t target = shadow + a.expected;
+        if (per_peer) {
+            uint64_t target = pp_shadow + a.expected;
             if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected && step == 1) target += 1;
-            const WaitResult res = sig_wait(&a.sig[(uint64_t)slot * kSignalStride], target, a.err,
-                                            a.timeout_ticks);
-            if (res.status == WAIT_TIMEOUT) record_timeout(a.err, ctx, r, step, target, res.observed);
-            shadow = target;
-            s_stop = res.status != WAIT_OK;
-            acquire_stores(local);
+            const PeerWait res = peer_wait(in_pp, peer_lane, target, a.err, a.timeout_ticks);
+            if (res.status == WAIT_TIMEOUT && lane == 0)
+                record_timeout(a.err, ctx, r, step, res.expected, res.observed,
+                               wrap(r + 1 + res.lane, a.R));
+            if (res.status != WAIT_OK) return;
+            pp_shadow = target;
+            if (lane == 0) acquire_stores(local);
+            __syncthreads();
+        } else {
+            if (lane == 0) {
+                uint64_t target = shadow + a.expected;
+                if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected && step == 1) target += 1;
+                const WaitResult res = sig_wait(&a.sig[(uint64_t)slot * kSignalStride], target,
+                                                a.err, a.timeout_ticks);
+                if (res.status == WAIT_TIMEOUT)
+                    record_timeout(a.err, ctx, r, step, target, res.observed);
+                shadow = target;
+                s_stop = res.status != WAIT_OK;
+                acquire_stores(local);
+            }
+            __syncthreads();
+            if (s_stop) return;
+            if (audit) {
+                bool missing = false;
+                if (peer_lane) {
+                    missing = !rolling_le(pp_shadow + 1, sig_read(in_pp));
+                    pp_shadow += 1;
+                }
+                if (__any(missing)) early += 1;
+            }
         }
-        __syncthreads();
-        if (s_stop) return;
+        if (defer && step == 2) {
+            arrive();
+            arrive();
+        }
     }
-    if (threadIdx.x == 0) a.shadow[slot] = shadow;
+    if (defer && a.nsteps == 1) arrive();
+    if (lane == 0) {
+        if (!per_peer) a.shadow[slot] = shadow;
+        if (audit) a.early[slot] += early;
+    }
+    if (use_pp && peer_lane) *in_pp_shadow = pp_shadow;
 }
 
 // ------------------------------------------------------ support kernels --
@@ -881,9 +994,13 @@ struct rr_counting_barrier {
     int nwaiters;
     int ncontexts;
     int device;
-    uint64_t* mem;     // signals (stride kSignalStride), then shadows
-    uint64_t* sig;
+    int pp_row;          // words per per-peer row: nwaiters rounded up to 128 bytes
+    uint64_t* mem;       // one allocation holding the arrays below
+    uint64_t* sig;       // counting signals, stride kSignalStride
     uint64_t* shadow;
+    uint64_t* pp_sig;    // per-peer slots, one row per (context, waiter)
+    uint64_t* pp_shadow;
+    uint64_t* early;     // early passes seen by audited runs
 };
 
 extern "C" {
@@ -956,7 +1073,8 @@ rr_status_t counting_barrier_create(int nwaiters, int ncontexts, rr_counting_bar
     int dev = 0;
     if (!hip_ok(hipGetDevice(&dev))) return RR_ERR_HIP;
     const size_t slots = (size_t)nwaiters * ncontexts;
-    const size_t words = slots * kSignalStride + slots;
+    const int pp_row = (int)round_up((uint64_t)nwaiters, 16);
+    const size_t words = slots * kSignalStride + slots + 2 * slots * pp_row + slots;
     void* p = nullptr;
     if (!hip_ok(hipMalloc(&p, words * sizeof(uint64_t)))) return RR_ERR_NOMEM;
     if (!hip_ok(hipMemset(p, 0, words * sizeof(uint64_t)))) {
@@ -971,9 +1089,13 @@ rr_status_t counting_barrier_create(int nwaiters, int ncontexts, rr_counting_bar
     b->nwaiters = nwaiters;
     b->ncontexts = ncontexts;
     b->device = dev;
+    b->pp_row = pp_row;
     b->mem = (uint64_t*)p;
     b->sig = b->mem;
-    b->shadow = b->mem + slots * kSignalStride;
+    b->shadow = b->sig + slots * kSignalStride;
+    b->pp_sig = b->shadow + slots;
+    b->pp_shadow = b->pp_sig + slots * pp_row;
+    b->early = b->pp_shadow + slots * pp_row;
     *out = b;
     return RR_OK;
 }
@@ -993,6 +1115,8 @@ rr_status_t counting_barrier_preset(rr_counting_barrier_t* b, uint64_t value, rr
     hipStream_t s = (hipStream_t)stream;
     rr_status_t st = fill(b->sig, slots, value, kSignalStride, s);
     if (st == RR_OK) st = fill(b->shadow, slots, value, 1, s);
+    if (st == RR_OK) st = fill(b->pp_sig, 2 * slots * b->pp_row, value, 1, s);  // with shadows
+    if (st == RR_OK) st = fill(b->early, slots, 0, 1, s);
     return st;
 }
 
@@ -1016,12 +1140,39 @@ rr_status_t counting_barrier_read(rr_counting_barrier_t* b, int ctx, int waiter,
     return RR_OK;
 }
 
+rr_status_t counting_barrier_read_peer(rr_counting_barrier_t* b, int ctx, int waiter, int peer,
+                                       uint64_t* value, uint64_t* shadow) {
+    if (!b || ctx < 0 || ctx >= b->ncontexts || waiter < 0 || waiter >= b->nwaiters ||
+        peer < 0 || peer >= b->nwaiters || peer == waiter)
+        return RR_ERR_INVALID;
+    if (!hip_ok(hipDeviceSynchronize())) return RR_ERR_HIP;
+    const size_t at = ((size_t)ctx * b->nwaiters + waiter) * b->pp_row + peer;
+    uint64_t v = 0, sh = 0;
+    if (!hip_ok(hipMemcpy(&v, b->pp_sig + at, sizeof v, hipMemcpyDeviceToHost))) return RR_ERR_HIP;
+    if (!hip_ok(hipMemcpy(&sh, b->pp_shadow + at, sizeof sh, hipMemcpyDeviceToHost)))
+        return RR_ERR_HIP;
+    if (value) *value = v;
+    if (shadow) *shadow = sh;
+    return RR_OK;
+}
+
+rr_status_t counting_barrier_early_passes(rr_counting_barrier_t* b, int ctx, int waiter,
+                                          uint64_t* count) {
+    if (!b || !count || ctx < 0 || ctx >= b->ncontexts || waiter < 0 || waiter >= b->nwaiters)
+        return RR_ERR_INVALID;
+    if (!hip_ok(hipDeviceSynchronize())) return RR_ERR_HIP;
+    const size_t at = (size_t)ctx * b->nwaiters + waiter;
+    return hip_ok(hipMemcpy(count, b->early + at, sizeof *count, hipMemcpyDeviceToHost))
+               ? RR_OK
+               : RR_ERR_HIP;
+}
+
 rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, int ncontexts,
                                  uint64_t expected_per_step, const rr_options_t* opt,
                                  rr_stream_t stream) {
     if (!b || R < 1 || R > b->nwaiters || ncontexts < 1 || ncontexts > b->ncontexts || nsteps < 0)
         return RR_ERR_INVALID;
-    if (opt && (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH)) return RR_ERR_INVALID;
+    if (opt && (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_PER_PEER)) return RR_ERR_INVALID;
     DeviceState* d = nullptr;
     rr_status_t st = ensure_device(&d);
     if (st != RR_OK) return st;
@@ -1031,6 +1182,10 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
     memset(&a, 0, sizeof a);
     a.sig = b->sig;
     a.shadow = b->shadow;
+    a.pp_sig = b->pp_sig;
+    a.pp_shadow = b->pp_shadow;
+    a.early = b->early;
+    a.pp_row = b->pp_row;
     a.xcc_table = d->xcc_table;
     a.err = d->err;
     a.nctx = ncontexts;
@@ -1044,8 +1199,11 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
     a.R = R;
     a.stride = b->nwaiters;
     a.nsteps = nsteps;
-    a.mode = opt && opt->sync == RR_SYNC_P2P ? SYNC_P2P : SYNC_BARRIER;
+    a.mode = !opt ? SYNC_BARRIER
+                  : opt->sync == RR_SYNC_P2P ? SYNC_P2P
+                  : opt->sync == RR_SYNC_PER_PEER ? SYNC_PER_PEER : SYNC_BARRIER;
     a.inject = opt ? opt->inject : 0;
+    a.audit = opt && (opt->flags & RR_FLAG_AUDIT) ? 1 : 0;
     void* args[] = {&a};
     hipStream_t s = (hipStream_t)stream;
     const bool coop = opt && (opt->flags & RR_FLAG_COOPERATIVE);
@@ -1076,6 +1234,7 @@ rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {
         rec->ctx = e.ctx;
         rec->waiter = e.waiter;
         rec->hop = e.hop;
+        rec->peer = e.peer;
         rec->expected = e.expected;
         rec->observed = e.observed;
     }

@@ -69,6 +69,7 @@ A = 0x7F0000000000  # 16-byte aligned addresses; never dereferenced by these tes
     dict(ptrs=[A, A + 32], count=16),                           # overlap (64 bytes each)
     dict(ptrs=[A + 4096, A, A + 4096 + 16], count=8),           # overlap after sorting
     dict(ptrs=[A, A + 4096], count=16, sync=9),
+    dict(ptrs=[A, A + 4096], count=16, sync="per_peer"),   # barrier runs only
     dict(ptrs=[A, A + 4096], count=16, block=128),
     dict(ptrs=[A, A + 4096], count=16, team=-1),
     dict(ptrs=[A, A + 4096], count=16, rounds=-1),
@@ -110,6 +111,9 @@ def test_counting_barrier_rejects_bad_shapes(rr):
     assert rr._cb_create(4, 1, None) == rr.RR_ERR_INVALID
     assert rr._cb_destroy(None) == rr.RR_OK
     assert rr._cb_run(None, 4, 1, 1, 3, None, None) == rr.RR_ERR_INVALID
+    n = ctypes.c_uint64()
+    assert rr._cb_read_peer(None, 0, 0, 1, ctypes.byref(n), ctypes.byref(n)) == rr.RR_ERR_INVALID
+    assert rr._cb_early(None, 0, 0, ctypes.byref(n)) == rr.RR_ERR_INVALID
 
 
 def test_copy_rejects_bad_arguments(rr):

@@ -100,6 +100,119 @@ def test_counting_barrier_injected_drop(rr):
     b.close()
 
 
+# ------------------------------------------- per-peer slots vs counting signal
+
+@pytest.mark.parametrize("R,nctx", [(2, 1), (8, 4), (64, 8)])
+def test_per_peer_barrier_counts(rr, R, nctx):
+    log(f"case per-peer counts R={R} nctx={nctx}")
+    b = rr.CountingBarrier(64, 8)
+    steps = 40
+    b.run(R, steps, nctx, mode="per_peer")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    for ctx in range(nctx):
+        for q in (0, R // 2, R - 1):
+            for p in {(q + 1) % R, (q + R - 1) % R}:
+                if p != q:
+                    assert b.read_peer(ctx, q, p) == (steps, steps)
+            assert b.read(ctx, q) == (0, 0)  # the counting signals are not used
+    b.run(R, 3, nctx, mode="per_peer")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert b.read_peer(0, R - 1, 0) == (steps + 3, steps + 3)
+    b.close()
+
+
+def test_per_peer_barrier_wraps(rr):
+    b = rr.CountingBarrier(8, 1)
+    start = (1 << 64) - 2
+    b.preset(start)
+    b.run(8, 6, 1, mode="per_peer")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert b.read_peer(0, 5, 2) == ((start + 6) % (1 << 64),) * 2
+    b.close()
+
+
+def test_per_peer_timeout_names_the_peer(rr):
+    """A per-peer slot knows who is missing; the record names that peer."""
+    log("case per-peer timeout")
+    b = rr.CountingBarrier(8, 1)
+    b.run(8, 3, 1, mode="per_peer", inject=rr.INJECT_DROP_ARRIVAL, timeout_ns=SHORT)
+    st, rec = rr.last_kernel_error()
+    assert st == rr.RR_ERR_TIMEOUT
+    assert 0 <= rec["peer"] < 8 and rec["peer"] != rec["waiter"]
+    value, _ = b.read_peer(rec["ctx"], rec["waiter"], rec["peer"])
+    assert value == rec["observed"] < rec["expected"]
+    # Rank 0 skipped its step-1 arrivals.  Its later arrivals still come from
+    # rank 0, so each slot lets the others through steps 1 and 2 one arrival
+    # late, and the shortfall shows at the last step, where the record names
+    # rank 0 as the missing peer.
+    assert rec["peer"] == 0 and rec["waiter"] != 0 and rec["hop"] == 3
+    for q in range(1, 8):
+        assert b.read_peer(0, q, 0)[0] == 2
+    b.close()
+
+
+@pytest.mark.parametrize("R", [3, 8, 64])
+def test_deferred_arrival_counting_passes_on_a_stand_in(rr, R):
+    """Waiter 0 holds back its step-1 and step-2 arrivals at waiter 1 until it
+    has passed step 2.  The counting barrier completes anyway: another peer one
+    step ahead fills waiter 1's step-1 count, which the audit witnesses record
+    as an early pass."""
+    log(f"case defer counting R={R}")
+    b = rr.CountingBarrier(64, 1)
+    steps = 6
+    b.run(R, steps, 1, mode="barrier", inject=rr.INJECT_DEFER_ARRIVAL, flags=rr.FLAG_AUDIT)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert b.early_passes(0, 1) >= 1
+    for q in range(R):
+        assert b.read(0, q) == (steps * (R - 1),) * 2
+    assert b.read_peer(0, 1, 0) == (steps, steps)  # every witness caught up by the end
+    b.close()
+
+
+@pytest.mark.parametrize("R,mode", [(3, "per_peer"), (8, "per_peer"), (2, "barrier")])
+def test_deferred_arrival_blocks_identity_barriers(rr, R, mode):
+    """Per-peer slots (and a counting barrier with a single peer) cannot pass
+    without that arrival: the held-back arrival never comes, the waits time out,
+    and the record names a waiter whose wait was truly unmet."""
+    log(f"case defer blocks R={R} mode={mode}")
+    b = rr.CountingBarrier(8, 1)
+    b.run(R, 4, 1, mode=mode, inject=rr.INJECT_DEFER_ARRIVAL, timeout_ns=SHORT)
+    st, rec = rr.last_kernel_error()
+    assert st == rr.RR_ERR_TIMEOUT
+    if mode == "per_peer":
+        value, _ = b.read_peer(rec["ctx"], rec["waiter"], rec["peer"])
+        assert value == rec["observed"] < rec["expected"]
+        assert b.read_peer(0, 1, 0)[0] == 0
+    else:
+        assert rec["peer"] == -1  # a counting signal cannot name the peer
+    b.close()
+
+
+def test_audit_without_injection(rr):
+    """Audited counting runs and per-peer runs keep every count exact; per-peer
+    runs never count early passes."""
+    R, steps = 16, 200
+    b = rr.CountingBarrier(16, 2)
+    b.run(R, steps, 2, mode="barrier", flags=rr.FLAG_AUDIT)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    for q in range(R):
+        assert b.read(1, q) == (steps * (R - 1),) * 2
+        assert b.read_peer(1, q, (q + 3) % R) == (steps, steps)
+    early = sum(b.early_passes(c, q) for c in range(2) for q in range(R))
+    log(f"audited counting barrier R={R}: {early} early passes in {2 * R * steps} waits")
+    b.reset()
+    b.run(R, steps, 2, mode="per_peer", flags=rr.FLAG_AUDIT)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert all(b.early_passes(c, q) == 0 for c in range(2) for q in range(R))
+    b.close()
+
+
 def _small_case(rr):
     R, count = 8, 8 * 20000 + 3
     x = workloads.generate(R, count, "fp32", "uniform_pm1", 31)
