@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--r16-sweep", action="store_true",
+                    help="R=16 fp32 size sweep, 4 KiB .. 1 GiB per rank: one JSON line per point")
     ap.add_argument("--barrier-latency", action="store_true",
                     help="instead of the AllReduce: per-step latency of the counting barrier "
                          "alone for R = 2..64 and 1 or 8 contexts (one JSON line per point)")
@@ -116,6 +118,8 @@ def main():
     torch.cuda.set_device(0)
     if args.barrier_latency:
         return barrier_latency(rr, torch)
+    if args.r16_sweep:
+        return r16_sweep(rr, torch, np)
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
@@ -299,6 +303,49 @@ def barrier_latency(rr, torch):
                           "contexts": nctx, "steps": asteps, "waits": nctx * R * asteps,
                           "early_passes": early}), flush=True)
     b.close()
+    return 0
+
+
+def r16_sweep(rr, torch, np):
+    """The R=16 fp32 sweep, 4 KiB * 4^k per rank (k = 0..9): SUM with 1, 4 and 16
+    slices and MAX with 4, each in barrier and p2p mode.  Per point: inputs
+    restored, 2 warm-up calls, then 10 calls timed with HIP events on the launch
+    stream; GB/s on the algorithmic bytes 5(R-1)N."""
+    import workloads
+    rr.init()
+    stream = torch.cuda.current_stream()
+    for k in range(10):
+        w0 = workloads.r16_sweep(k, "sum", 4)
+        x = workloads.inputs(w0)
+        slabs = rr.make_slabs(w0.R, w0.count, torch.float32, device="cuda")
+        for r in range(w0.R):
+            slabs.ranks[r].copy_(torch.from_numpy(x[r]))
+        del x
+        pristine = slabs.storage.clone()
+        for op, ns in (("sum", 1), ("sum", 4), ("sum", 16), ("max", 4)):
+            for sync in ("barrier", "p2p"):
+                p = rr.plan(w0.R, w0.count, "fp32", ns, sync=sync)
+                slabs.storage.copy_(pristine)
+                for _ in range(2):
+                    rr.allreduce_ring(slabs.ranks, op, ns, sync=sync)
+                a = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(10):
+                    rr.allreduce_ring(slabs.ranks, op, ns, sync=sync)
+                e.record(stream)
+                torch.cuda.synchronize()
+                rr.check_kernel_error()
+                ms = a.elapsed_time(e) / 10
+                B = p["hbm_bytes"]
+                print(json.dumps({"metric": "R=16 fp32 sweep", "bytes_per_rank": w0.bytes_per_rank,
+                                  "op": op, "nslices": ns, "sync": p["sync"], "ms": round(ms, 5),
+                                  "GB/s": round(B / ms / 1e6, 1),
+                                  "pct_of_peak": round(100 * B / ms / 1e6 / HBM_PEAK_GBS, 2),
+                                  "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],
+                                  "grid": p["grid"], "launches": p["launches"]}), flush=True)
+        del slabs, pristine
+        torch.cuda.empty_cache()
     return 0
 
 

@@ -855,14 +855,25 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
         rounds = (int)std::max<uint64_t>(1, ceil_div(hop_bytes, kRoundBytes));
     }
     int team;
+    const uint64_t slice_vecs = p->slice_len / V;
+    const uint64_t min_vecs = (uint64_t)block * 4;  // one unrolled pass per hop
+    const uint64_t by_size = std::max<uint64_t>(1, slice_vecs / min_vecs);
+    auto auto_team = [&](int dd) {
+        const uint64_t wanted = ceil_div((uint64_t)target_cols * dd * rounds, nslices);
+        return (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
+    };
     if (opt && opt->team > 0) {
         team = opt->team;
     } else {
-        const uint64_t slice_vecs = p->slice_len / V;
-        const uint64_t min_vecs = (uint64_t)block * 4;  // one unrolled pass per hop
-        const uint64_t by_size = std::max<uint64_t>(1, slice_vecs / min_vecs);
-        const uint64_t wanted = ceil_div((uint64_t)target_cols * depth * rounds, nslices);
-        team = (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
+        team = auto_team(depth);
+        // Interleaving pays only when the buffer can fill at least half the
+        // columns wanted; a smaller one would just serialise two lanes'
+        // hand-offs in one workgroup (R=16: 4 MiB per rank and below).
+        if (!fixed_depth && depth > 1 &&
+            2 * (uint64_t)nslices * team / ((uint64_t)depth * rounds) < (uint64_t)target_cols) {
+            depth = 1;
+            team = auto_team(1);
+        }
     }
     // every lane needs R signals in the workspace
     const int max_team = std::max(1, kSlots / (R * nslices));
