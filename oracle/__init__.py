@@ -9,7 +9,7 @@ simulator); this module loads it with ctypes and adds numpy-facing wrappers plus
 the primitive labels of one ring loop derived from the recorded hops.
 
 Arrays: int32 -> ``np.int32``, fp32 -> ``np.float32``, bf16 -> ``np.uint16``
-holding the raw bfloat16 bit patterns.
+holding the raw bfloat16 bit patterns, fp16 -> ``np.float16``.
 """
 from __future__ import annotations
 
@@ -25,9 +25,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ring_oracle.c")
 _LIB = os.path.join(_HERE, "libring_oracle.so")
 
-DTYPES = {"int32": 0, "fp32": 1, "bf16": 2}
-NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "bf16": np.uint16}
-OPS = {"sum": 0, "max": 1}
+DTYPES = {"int32": 0, "fp32": 1, "bf16": 2, "fp16": 3}
+NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "bf16": np.uint16, "fp16": np.float16}
+OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
+PRIMITIVES = ["send", "recvReduceSend", "recvReduceCopySend", "recvCopySend", "recv",
+              "recvReduceCopy", "copySend"]
 MAX_RANKS = 64
 
 _lock = threading.Lock()
@@ -52,6 +54,17 @@ class _Hop(ctypes.Structure):
                 ("terms", ctypes.c_uint8 * MAX_RANKS)]
 
 
+class _Step(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("rank", ctypes.c_int32), ("prim", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("bytes_read", ctypes.c_uint64),
+                ("bytes_written", ctypes.c_uint64)]
+
+
+class _StepLog(ctypes.Structure):
+    _fields_ = [("steps", ctypes.POINTER(_Step)), ("capacity", ctypes.c_int32),
+                ("used", ctypes.c_int32)]
+
+
 class _Trace(ctypes.Structure):
     _fields_ = [("hops", ctypes.POINTER(_Hop)), ("capacity", ctypes.c_int32),
                 ("used", ctypes.c_int32)]
@@ -65,8 +78,14 @@ def _bind(lib):
     lib.ro_all_gather.argtypes = [ctypes.POINTER(vp), i32, u64, i32, ctypes.POINTER(_Trace)]
     lib.ro_allreduce_at.argtypes = [vp, vp, u64, i32, i32, i32, vp]
     lib.ro_direct_sum_f64.argtypes = [ctypes.POINTER(vp), i32, u64, i32, vp, vp]
+    lib.ro_staged_allreduce.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, u64, i32, i32,
+                                        ctypes.POINTER(_StepLog)]
+    lib.ro_reduce_scatter_nccl.argtypes = lib.ro_staged_allreduce.argtypes
+    lib.ro_all_gather_nccl.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, u64, i32,
+                                       ctypes.POINTER(_StepLog)]
     for f in (lib.ro_chunk_bounds, lib.ro_allreduce, lib.ro_reduce_scatter, lib.ro_all_gather,
-              lib.ro_allreduce_at, lib.ro_direct_sum_f64):
+              lib.ro_allreduce_at, lib.ro_direct_sum_f64, lib.ro_staged_allreduce,
+              lib.ro_reduce_scatter_nccl, lib.ro_all_gather_nccl):
         f.restype = ctypes.c_int
     return lib
 
@@ -75,8 +94,7 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
-                build()
+            build()  # rebuilds only when the source is newer than the library
             _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
 
@@ -235,3 +253,72 @@ def primitive_labels(hops, R: int):
             seq.append(name)
         labels[rank] = seq
     return labels
+
+
+@dataclass
+class Step:
+    step: int
+    rank: int
+    prim: str
+    chunk: int
+    bytes_read: int
+    bytes_written: int
+
+
+def _staged(fn, send, recv, n, args, log: bool):
+    R = len(send)
+    sp = (ctypes.c_void_p * R)(*[b.ctypes.data for b in send])
+    rp = (ctypes.c_void_p * R)(*[b.ctypes.data for b in recv])
+    lg = None
+    if log:
+        cap = 2 * R * R
+        steps = (_Step * cap)()
+        lg = _StepLog(ctypes.cast(steps, ctypes.POINTER(_Step)), cap, 0)
+    _check(fn(sp, rp, R, n, *args, ctypes.byref(lg) if lg is not None else None), fn.__name__)
+    if not log:
+        return None
+    return [Step(s.step, s.rank, PRIMITIVES[s.prim], s.chunk, int(s.bytes_read),
+                 int(s.bytes_written)) for s in (lg.steps[k] for k in range(min(lg.used, lg.capacity)))]
+
+
+def _contig(bufs, n, dtype):
+    for b in bufs:
+        if not b.flags.c_contiguous or b.dtype != NP_DTYPES[dtype] or b.size != n:
+            raise ValueError("buffers must be contiguous arrays of the right dtype and length")
+
+
+def staged_allreduce(send, op: str = "sum", recv=None, log: bool = False):
+    """The staged loop of Table V, out of place.  Returns (recv, steps)."""
+    dt = _dtype_of(send)
+    n = send[0].size
+    _contig(send, n, dt)
+    if recv is None:
+        recv = [np.zeros_like(b) for b in send]
+    _contig(recv, n, dt)
+    steps = _staged(_load().ro_staged_allreduce, send, recv, n, (DTYPES[dt], OPS[op]), log)
+    return recv, steps
+
+
+def reduce_scatter_nccl(send, op: str = "sum", log: bool = False):
+    """send[r] holds R blocks; returns (recv, steps), recv[r] = block r reduced."""
+    dt = _dtype_of(send)
+    R = len(send)
+    total = send[0].size
+    if total % R:
+        raise ValueError("send buffers must hold R equal blocks")
+    _contig(send, total, dt)
+    n = total // R
+    recv = [np.zeros(n, dtype=NP_DTYPES[dt]) for _ in range(R)]
+    steps = _staged(_load().ro_reduce_scatter_nccl, send, recv, n, (DTYPES[dt], OPS[op]), log)
+    return recv, steps
+
+
+def all_gather_nccl(send, log: bool = False):
+    """send[r] holds one block; returns (recv, steps), recv[r] = all R blocks."""
+    dt = _dtype_of(send)
+    R = len(send)
+    n = send[0].size
+    _contig(send, n, dt)
+    recv = [np.zeros(R * n, dtype=NP_DTYPES[dt]) for _ in range(R)]
+    steps = _staged(_load().ro_all_gather_nccl, send, recv, n, (DTYPES[dt],), log)
+    return recv, steps

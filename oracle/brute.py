@@ -16,6 +16,10 @@ ring result:
 Values are Python ints for int32 (wrapped to 32 bits after each addition) and
 ``Fraction`` for floating point, so nothing here shares rounding behaviour with
 the C oracle.
+
+The other reductions follow the same fold: MAX keeps the running value unless
+the next rank's compares greater, MIN unless it compares less; PROD multiplies
+exactly and rounds once to the format (int32 wraps).
 """
 from __future__ import annotations
 
@@ -24,7 +28,7 @@ import struct
 from fractions import Fraction
 
 # (significant bits, minimum normal exponent, maximum exponent)
-FORMATS = {"fp32": (24, -126, 127), "bf16": (8, -126, 127)}
+FORMATS = {"fp32": (24, -126, 127), "bf16": (8, -126, 127), "fp16": (11, -14, 15)}
 
 INF = float("inf")
 
@@ -39,6 +43,23 @@ def fp32_bits_to_value(bits: int):
 
 def bf16_bits_to_value(bits: int):
     return fp32_bits_to_value((bits & 0xFFFF) << 16)
+
+
+def fp16_bits_to_value(bits: int):
+    x = struct.unpack("<e", struct.pack("<H", bits & 0xFFFF))[0]
+    if math.isnan(x) or math.isinf(x) or x == 0.0:
+        return x
+    return Fraction(x)
+
+
+def value_to_fp16_bits(v) -> int:
+    if isinstance(v, float) and math.isnan(v):
+        return 0x7E00
+    if isinstance(v, Fraction):
+        f = float(v)
+        assert Fraction(f) == v
+        v = f
+    return struct.unpack("<H", struct.pack("<e", v))[0]
 
 
 def value_to_fp32_bits(v) -> int:
@@ -106,6 +127,32 @@ def add(a, b, fmt: str):
     return round_nearest_even(s, fmt)
 
 
+def mul(a, b, fmt: str):
+    """One IEEE multiplication in the format: exact product, then one rounding."""
+    fa = isinstance(a, float)
+    fb = isinstance(b, float)
+    if (fa and math.isnan(a)) or (fb and math.isnan(b)):
+        return math.nan
+    sa = math.copysign(1, a) if fa else (1 if a > 0 else -1)
+    sb = math.copysign(1, b) if fb else (1 if b > 0 else -1)
+    sign = sa * sb
+    a_inf = fa and math.isinf(a)
+    b_inf = fb and math.isinf(b)
+    a_zero = fa and a == 0.0
+    b_zero = fb and b == 0.0
+    if (a_inf and b_zero) or (b_inf and a_zero):
+        return math.nan
+    if a_inf or b_inf:
+        return sign * INF
+    if a_zero or b_zero:
+        return math.copysign(0.0, sign)
+    p = a * b
+    r = round_nearest_even(p, fmt)
+    if r == 0:
+        return math.copysign(0.0, sign)
+    return r
+
+
 def ring_order(R: int, chunk: int):
     """Ranks in the order the ring folds an element of ``chunk``."""
     return [(chunk + i) % R for i in range(R)]
@@ -119,20 +166,24 @@ def allreduce_element(values, chunk: int, dtype: str, op: str):
         xs = [int(values[r]) for r in order]
         if op == "max":
             return max(xs)
-        acc = 0
-        for x in xs:
-            acc = (acc + x) & 0xFFFFFFFF
+        if op == "min":
+            return min(xs)
+        acc = xs[0] & 0xFFFFFFFF
+        for x in xs[1:]:
+            acc = (acc * x if op == "prod" else acc + x) & 0xFFFFFFFF
         return acc - (1 << 32) if acc >= (1 << 31) else acc
-    decode = fp32_bits_to_value if dtype == "fp32" else bf16_bits_to_value
-    encode = value_to_fp32_bits if dtype == "fp32" else value_to_bf16_bits
+    decode = {"fp32": fp32_bits_to_value, "bf16": bf16_bits_to_value,
+              "fp16": fp16_bits_to_value}[dtype]
+    encode = {"fp32": value_to_fp32_bits, "bf16": value_to_bf16_bits,
+              "fp16": value_to_fp16_bits}[dtype]
     xs = [decode(int(values[r])) for r in order]
-    if op == "max":
+    if op in ("max", "min"):
         best = xs[0]
         for x in xs[1:]:
-            if x > best:
+            if (x > best) if op == "max" else (x < best):
                 best = x
         return encode(best)
     acc = xs[0]
     for x in xs[1:]:
-        acc = add(acc, x, dtype)
+        acc = add(acc, x, dtype) if op == "sum" else mul(acc, x, dtype)
     return encode(acc)

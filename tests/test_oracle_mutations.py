@@ -13,7 +13,9 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_ops as ops
 from tests import test_oracle_pins as pins
+from tests import test_oracle_staged as staged
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -39,7 +41,29 @@ MUTANTS = [
     ("bf16_flushes_subnormals", "if (q < -133) q = -133;", "if (q < -126) q = -126;", 0),
     ("bf16_keeps_9_bits", "int q = e - 8;", "int q = e - 9;", 0),
     ("bf16_overflow_early", "if (r >= 0x1p128)", "if (r >= 0x1p127)", 0),
-    ("bf16_max_is_min", "lo[i] = b > a ? lo[i] : in[i];", "lo[i] = b > a ? in[i] : lo[i];", 0),
+    ("bf16_max_is_min", "lo[i] = b > a ? lo[i] : in[i];", "lo[i] = b > a ? in[i] : lo[i];", 1),
+    ("fp16_max_is_min", "lo[i] = b > a ? lo[i] : in[i];", "lo[i] = b > a ? in[i] : lo[i];", 0),
+    ("fp16_truncates", "double r = ldexp(nearbyint(ldexp(a, -q)), q);",
+     "double r = ldexp(floor(ldexp(a, -q)), q);", 0),
+    ("fp16_flushes_subnormals", "if (q < -24) q = -24;", "if (q < -14) q = -14;", 0),
+    ("fp16_overflow_early", "if (r > 65504.0)", "if (r >= 65504.0)", 0),
+    ("fp16_keeps_12_bits", "int q = e - 11;", "int q = e - 12;", 0),
+    ("fp16_nan_payload", "if (isnan(x)) return 0x7E00u;", "if (isnan(x)) return 0x7E01u;", 0),
+    ("int_min_is_max", "lo[i] = lo[i] < in[i] ? lo[i] : in[i];", "lo[i] = lo[i] < in[i] ? in[i] : lo[i];", 0),
+    ("fp32_min_is_max", "lo[i] = lo[i] < in[i] ? lo[i] : in[i];", "lo[i] = lo[i] < in[i] ? in[i] : lo[i];", 1),
+    ("fp16_min_is_max", "lo[i] = b < a ? lo[i] : in[i];", "lo[i] = b < a ? in[i] : lo[i];", 0),
+    ("bf16_min_is_max", "lo[i] = b < a ? lo[i] : in[i];", "lo[i] = b < a ? in[i] : lo[i];", 1),
+    ("int_prod_adds", "(uint32_t)in[i] * (uint32_t)lo[i]", "(uint32_t)in[i] + (uint32_t)lo[i]", 0),
+    ("fp32_prod_squares", "lo[i] = in[i] * lo[i];", "lo[i] = lo[i] * lo[i];", 0),
+    ("fp16_prod_is_sum", "lo[i] = fp16_from_double(a * b);", "lo[i] = fp16_from_double(a + b);", 0),
+    ("bf16_prod_truncates", "lo[i] = bf16_from_double(a * b);", "lo[i] = bf16_from_double(a * b * 0x1.0000001p0);", 0),
+    ("staged_reads_wrong_slot", "(size_t)((k + 1) & 1)", "(size_t)(k & 1)", 0),
+    ("staged_chunk_schedule", "int c = mod(r - k - (mode == STAGED_RS ? 1 : 0), R);",
+     "int c = mod(r + k - (mode == STAGED_RS ? 1 : 0), R);", 0),
+    ("rs_nccl_unshifted", "(mode == STAGED_RS ? 1 : 0)", "(mode == STAGED_RS ? 0 : 0)", 0),
+    ("staged_copy_late", "has_out = k >= R - 1;", "has_out = k >= R;", 0),
+    ("staged_reduces_in_allgather", "reduce = k >= 1 && k <= R - 1;", "reduce = k >= 1;", 0),
+    ("ag_nccl_skips_own_block", "has_out = 1;", "has_out = k >= 1;", 0),
     ("bf16_nan_payload", "if (isnan(x)) return 0x7FC0u;", "if (isnan(x)) return 0x7FC1u;", 0),
     ("ag_reduces", "memcpy((char *)bufs[q] + lo * es, (const char *)bufs[r] + lo * es, n * es);",
      "fold_range(dt, RO_MAX, (const char *)bufs[r] + lo * es, (char *)bufs[q] + lo * es, n);", 0),
@@ -73,6 +97,28 @@ def _pin_suite():
         lambda: pins.test_partition(100, 8, "bf16"),
         pins.test_edge_cases,
         pins.test_int32_wraps,
+        lambda: ops.test_min_prod_brute_force("int32", "min", 5, 37),
+        lambda: ops.test_min_prod_brute_force("fp32", "min", 5, 37),
+        lambda: ops.test_min_prod_brute_force("bf16", "min", 5, 37),
+        lambda: ops.test_min_prod_brute_force("fp16", "min", 5, 37),
+        lambda: ops.test_min_prod_brute_force("int32", "prod", 5, 37),
+        lambda: ops.test_min_prod_brute_force("fp32", "prod", 5, 37),
+        lambda: ops.test_min_prod_brute_force("bf16", "prod", 5, 37),
+        lambda: ops.test_min_prod_brute_force("fp16", "prod", 5, 37),
+        lambda: ops.test_fp16_sum_max_brute_force("sum", 4, 64),
+        lambda: ops.test_fp16_sum_max_brute_force("max", 4, 64),
+        lambda: ops.test_fp16_hop_is_correctly_rounded("sum", 3000),
+        lambda: ops.test_fp16_hop_is_correctly_rounded("prod", 3000),
+        ops.test_fp16_special_values,
+        lambda: ops.test_bf16_product_is_correctly_rounded(3000),
+        lambda: staged.test_staged_primitives_table_v_k4(GOLDEN),
+        lambda: staged.test_staged_chunks_follow_the_worked_example(GOLDEN),
+        lambda: staged.test_staged_traffic("fp32", 5, 37 * 5 + 3),
+        lambda: staged.test_staged_allreduce_brute_force("fp32", "sum", 5, 37),
+        lambda: staged.test_staged_allreduce_brute_force("int32", "max", 4, 64),
+        lambda: staged.test_reduce_scatter_nccl_brute_force("fp32", "sum", 5, 4),
+        lambda: staged.test_all_gather_nccl_is_the_gather("fp16", 5, 17),
+        lambda: staged.test_all_gather_nccl_is_the_gather("int32", 3, 5),
     ]
 
 

@@ -28,8 +28,8 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "bf16": np.uint16}
-ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
+NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "bf16": np.uint16, "fp16": np.float16}
+ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2, "fp16": 2}
 
 
 @dataclass(frozen=True)
@@ -84,6 +84,12 @@ def _draw(dist: str, dtype: str, count: int, rank: int, seed: int) -> np.ndarray
         x -= 1.0
     elif dist == "normal":
         x = rng.standard_normal(count, dtype=np.float32)
+    elif dist == "unit_jitter":      # magnitudes in [7/8, 9/8), random sign: long products stay finite
+        x = rng.random(count, dtype=np.float32)
+        x = (x - np.float32(0.5)) * np.float32(0.25) + np.float32(1.0)
+        x *= np.where(rng.random(count) < 0.5, np.float32(-1.0), np.float32(1.0)).astype(np.float32)
+        if dtype == "int32":
+            x = rng.integers(-3, 4, size=count, dtype=np.int32)
     elif dist == "onehot":           # rank r contributes the single bit 1 << r
         x = np.full(count, 1 << rank, dtype=np.int64)
     elif dist == "rank_index":       # rank r, position i holds r*1000 + i
@@ -94,6 +100,8 @@ def _draw(dist: str, dtype: str, count: int, rank: int, seed: int) -> np.ndarray
         x = rng.integers(0, 1 << 32, size=count, dtype=np.uint32)
         if dtype == "bf16":
             return (x & 0xFFFF).astype(np.uint16)
+        if dtype == "fp16":
+            return (x & 0xFFFF).astype(np.uint16).view(np.float16)
         return x.view(NP_DTYPES[dtype])
     else:
         raise ValueError(f"unknown distribution {dist!r}")
@@ -105,6 +113,8 @@ def _as_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
         return x.astype(np.int32, copy=False)
     if dtype == "fp32":
         return x.astype(np.float32, copy=False)
+    if dtype == "fp16":
+        return x.astype(np.float32, copy=False).astype(np.float16)  # round to nearest even
     import torch  # the cast below is torch's round-to-nearest-even conversion
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
