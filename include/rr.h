@@ -28,12 +28,13 @@
  * slices only schedule work: results do not depend on nslices.
  *
  * ARITHMETIC, one fold per ReduceScatter hop, local = incoming (op) local:
- *   int32 SUM  wraps modulo 2^32          int32 MAX  signed comparison
- *   fp32  SUM  one binary32 addition,     fp32  MAX  the local value if it
- *              round to nearest even                 compares greater, else
- *   bf16  SUM  the exact sum rounded to              the incoming value
- *              bf16, nearest even; a NaN  bf16  MAX  as fp32 MAX, keeping the
- *              result is 0x7FC0                      winner's bits
+ *   int32 SUM / PROD  wrap modulo 2^32
+ *   fp32  SUM / PROD  one binary32 operation, round to nearest even
+ *   bf16, fp16 SUM / PROD  the exact result rounded once to the format, nearest
+ *              even (computed in binary32 and rounded: the same bits); a NaN
+ *              result is 0x7FC0 (bf16) or 0x7E00 (fp16)
+ *   MAX / MIN  the local value if it compares greater / less, else the
+ *              incoming value, keeping the winner's bits (signed for int32)
  * So the element result of chunk c is the left fold over ranks c, c+1, ...,
  * c+R-1 (mod R), rounded to the storage type after every step.
  *
@@ -78,9 +79,9 @@ extern "C" {
 #define RR_MAX_RANKS 64      /* virtual ranks per call */
 #define RR_MAX_SLICES 1024   /* slices per call; slices * team * R <= 65536 */
 
-typedef enum { RR_INT32 = 0, RR_FP32 = 1, RR_BF16 = 2 } rr_dtype_t;
+typedef enum { RR_INT32 = 0, RR_FP32 = 1, RR_BF16 = 2, RR_FP16 = 3 } rr_dtype_t;
 
-typedef enum { RR_SUM = 0, RR_MAX = 1 } rr_op_t;
+typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2, RR_PROD = 3 } rr_op_t;
 
 typedef enum {
     RR_OK = 0,
@@ -231,8 +232,52 @@ rr_status_t reduce_scatter_ring_ex(void *const *bufs, int R, size_t count, rr_dt
 rr_status_t all_gather_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_t dt,
                                int nslices, const rr_options_t *opt, rr_stream_t stream);
 
+/* ------------------------------------------------- the staged, out-of-place loop */
+
+/* AllReduce as the staged primitives of Table V (the loosp.cn post, sections
+   8-10): at step k rank r handles chunk (r - k) mod R -- step 0 send, steps
+   1..R-2 recvReduceSend, step R-1 recvReduceCopySend, steps R..2R-3
+   recvCopySend, step 2R-2 recv.  Out of place: sendbufs[r] (count elements) is
+   only read; recvbufs[r] receives the result, the same bits as allreduce_ring
+   (same chunks, same fold order).  recvbufs[r] == sendbufs[r] is allowed (in
+   place); any other overlap is not.  Messages travel through library-owned
+   receive buffers of two chunk-sized slots per rank (2 * count elements in
+   all, allocated on first use and grown on demand; not under stream capture),
+   handed off by a `ready` signal per (lane, rank) and returned by a `credit`
+   signal, so traffic is (6R - 4) * count * elem bytes instead of the in-place
+   ring's 5(R - 1).  Options: sync AUTO, P2P or LAUNCH (BARRIER is
+   RR_ERR_UNSUPPORTED), team, timeout_ns, inject, flags; block must be 0 or 512.
+   Errors: as allreduce_ring, plus RR_ERR_INVALID for overlapping buffers. */
+rr_status_t allreduce_ring_staged(const void *const *sendbufs, void *const *recvbufs, int R,
+                                  size_t count, rr_dtype_t dt, rr_op_t op, int nslices,
+                                  const rr_options_t *opt, rr_stream_t stream);
+
+/* ReduceScatter with the standalone collective's numbering (the loosp.cn post,
+   section 2: which rank keeps which reduced chunk is a matter of numbering).
+   sendbufs[r] holds R blocks of recvcount elements, block q at element
+   q * recvcount; recvbufs[r] (recvcount elements) receives block r reduced
+   over all ranks, folded around the ring from rank r+1: the staged loop
+   shifted by one chunk (send, recvReduceSend x (R-2), recvReduceCopy).  Any
+   recvcount; buffers 16-byte aligned and pairwise disjoint.  Traffic
+   (3R - 1) * R * recvcount * elem bytes.  Options and errors as
+   allreduce_ring_staged. */
+rr_status_t reduce_scatter(const void *const *sendbufs, void *const *recvbufs, int R,
+                           size_t recvcount, rr_dtype_t dt, rr_op_t op, int nslices,
+                           const rr_options_t *opt, rr_stream_t stream);
+
+/* AllGather (the loosp.cn post, section 3): sendbufs[r] holds sendcount
+   elements; recvbufs[r] receives R blocks, block q = sendbufs[q], bit for bit
+   (copySend, recvCopySend x (R-2), recv).  Any sendcount; buffers 16-byte
+   aligned and pairwise disjoint.  Traffic (3R - 1) * R * sendcount * elem
+   bytes.  Options and errors as allreduce_ring_staged. */
+rr_status_t all_gather(const void *const *sendbufs, void *const *recvbufs, int R,
+                       size_t sendcount, rr_dtype_t dt, int nslices, const rr_options_t *opt,
+                       rr_stream_t stream);
+
 /* The plan a call with these arguments would run; no device work.  `phase` is
-   0 for AllReduce, 1 for ReduceScatter, 2 for AllGather.  Errors as the call. */
+   0 for AllReduce, 1 for ReduceScatter, 2 for AllGather (the in-place ring),
+   3 for allreduce_ring_staged, 4 for reduce_scatter (count = recvcount), 5 for
+   all_gather (count = sendcount).  Errors as the call. */
 rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int phase,
                           const rr_options_t *opt, rr_plan_t *out);
 

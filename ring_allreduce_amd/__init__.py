@@ -30,11 +30,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 RR_MAX_RANKS = 64
 RR_MAX_SLICES = 1024
 
-DTYPES = {"int32": 0, "fp32": 1, "bf16": 2}
-OPS = {"sum": 0, "max": 1}
+DTYPES = {"int32": 0, "fp32": 1, "bf16": 2, "fp16": 3}
+OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
 SYNCS = {"auto": 0, "p2p": 1, "barrier": 2, "launch": 3, "per_peer": 4}
 SYNC_NAMES = {v: k for k, v in SYNCS.items()}
-PHASES = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+PHASES = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "allreduce_staged": 3,
+          "reduce_scatter_blocks": 4, "all_gather_blocks": 5}
 
 STATUS = {0: "RR_OK", 1: "RR_ERR_INVALID", 2: "RR_ERR_UNSUPPORTED", 3: "RR_ERR_HIP",
           4: "RR_ERR_TIMEOUT", 5: "RR_ERR_NOMEM"}
@@ -49,8 +50,9 @@ FLAG_COOPERATIVE = 0x4
 FLAG_FUSED_BOUNDARY = 0x8
 FLAG_AUDIT = 0x10
 
-_TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16"}
-ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
+_TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16",
+                 torch.float16: "fp16"}
+ELEM_BYTES = {"int32": 4, "fp32": 4, "bf16": 2, "fp16": 2}
 
 
 class Options(ctypes.Structure):
@@ -103,6 +105,12 @@ _allreduce_ring = _sig("allreduce_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _
 _reduce_scatter_ring = _sig("reduce_scatter_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _vp)
 _all_gather_ring = _sig("all_gather_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _vp)
 _plan_query = _sig("rr_plan_query", _i, _i, _sz, _i, _i, _i, _OPT, ctypes.POINTER(_Plan))
+_allreduce_ring_staged = _sig("allreduce_ring_staged", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                              _i, _sz, _i, _i, _i, _OPT, _vp)
+_reduce_scatter = _sig("reduce_scatter", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i,
+                       _i, _i, _OPT, _vp)
+_all_gather = _sig("all_gather", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i, _i,
+                   _OPT, _vp)
 _cb_create = _sig("counting_barrier_create", _i, _i, _i, ctypes.POINTER(_vp))
 _cb_destroy = _sig("counting_barrier_destroy", _i, _vp)
 _cb_reset = _sig("counting_barrier_reset", _i, _vp, _vp)
@@ -122,7 +130,8 @@ _finalize = _sig("rr_finalize", None)
 
 # Every symbol include/rr.h declares, for the export check.
 EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
-            "reduce_scatter_ring_ex", "all_gather_ring_ex", "rr_plan_query",
+            "reduce_scatter_ring_ex", "all_gather_ring_ex", "allreduce_ring_staged",
+            "reduce_scatter", "all_gather", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
             "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
             "counting_barrier_early_passes", "counting_barrier_run",
@@ -177,7 +186,7 @@ def _buffers(tensors):
         raise ValueError("need at least one rank buffer")
     t0 = tensors[0]
     if t0.dtype not in _TORCH_DTYPES:
-        raise TypeError(f"unsupported dtype {t0.dtype}; use int32, float32 or bfloat16")
+        raise TypeError(f"unsupported dtype {t0.dtype}; use int32, float32, bfloat16 or float16")
     for t in tensors:
         if t.device.type != "cuda" or t.device != t0.device:
             raise ValueError("all rank buffers must be on the same GPU")
@@ -229,6 +238,90 @@ def all_gather_ring(tensors, nslices: int = 1, *, stream=None, **opts) -> None:
         else:
             st = _all_gather_ring(ptrs, len(tensors), count, DTYPES[dt], nslices, s)
     _check(st, "all_gather_ring")
+
+
+def _pair(send, recv, send_elems, recv_elems):
+    """Pointer arrays for send/receive tensor lists (same device, dtype, sizes)."""
+    if not send or len(send) != len(recv):
+        raise ValueError("need one send and one receive buffer per rank")
+    t0 = send[0]
+    if t0.dtype not in _TORCH_DTYPES:
+        raise TypeError(f"unsupported dtype {t0.dtype}")
+    for t, n in [(t, send_elems) for t in send] + [(t, recv_elems) for t in recv]:
+        if t.device.type != "cuda" or t.device != t0.device or t.dtype != t0.dtype:
+            raise ValueError("all buffers must be on the same GPU with the same dtype")
+        if t.numel() != n or not t.is_contiguous():
+            raise ValueError("buffer has the wrong length or is not contiguous")
+    sp = (ctypes.c_void_p * len(send))(*[t.data_ptr() for t in send])
+    rp = (ctypes.c_void_p * len(recv))(*[t.data_ptr() for t in recv])
+    return sp, rp, _TORCH_DTYPES[t0.dtype]
+
+
+def allreduce_ring_staged(send, recv=None, op: str = "sum", nslices: int = 1, *, stream=None,
+                          **opts):
+    """Out-of-place AllReduce by the staged primitives (recv defaults to new
+    tensors; pass recv=send for in place).  Returns recv."""
+    if recv is None:
+        recv = [torch.empty_like(t) for t in send]
+    n = send[0].numel()
+    sp, rp, dt = _pair(send, recv, n, n)
+    with torch.cuda.device(send[0].device):
+        o = _options(**opts)
+        st = _allreduce_ring_staged(sp, rp, len(send), n, DTYPES[dt], OPS[op], nslices,
+                                    ctypes.byref(o), _stream_handle(stream))
+    _check(st, "allreduce_ring_staged")
+    return recv
+
+
+def reduce_scatter(send, recv=None, op: str = "sum", nslices: int = 1, *, stream=None, **opts):
+    """Standalone ReduceScatter: send[r] holds R blocks; recv[r] gets block r
+    reduced over all ranks.  Returns recv."""
+    R = len(send)
+    total = send[0].numel()
+    if total % R:
+        raise ValueError("send buffers must hold R equal blocks")
+    n = total // R
+    if recv is None:
+        recv = [torch.empty(n, dtype=send[0].dtype, device=send[0].device) for _ in range(R)]
+    sp, rp, dt = _pair(send, recv, total, n)
+    with torch.cuda.device(send[0].device):
+        o = _options(**opts)
+        st = _reduce_scatter(sp, rp, R, n, DTYPES[dt], OPS[op], nslices, ctypes.byref(o),
+                             _stream_handle(stream))
+    _check(st, "reduce_scatter")
+    return recv
+
+
+def all_gather(send, recv=None, nslices: int = 1, *, stream=None, **opts):
+    """Standalone AllGather: recv[r] gets all R send blocks in rank order.
+    Returns recv."""
+    R = len(send)
+    n = send[0].numel()
+    if recv is None:
+        recv = [torch.empty(R * n, dtype=send[0].dtype, device=send[0].device) for _ in range(R)]
+    sp, rp, dt = _pair(send, recv, n, R * n)
+    with torch.cuda.device(send[0].device):
+        o = _options(**opts)
+        st = _all_gather(sp, rp, R, n, DTYPES[dt], nslices, ctypes.byref(o),
+                         _stream_handle(stream))
+    _check(st, "all_gather")
+    return recv
+
+
+def staged_ptrs(kind: str, send, recv, n: int, dtype, op="sum", nslices: int = 1, stream=0,
+                **opts) -> int:
+    """Raw-pointer call of the staged entry points; returns the status."""
+    R = len(send) if send is not None else 0
+    sp = (ctypes.c_void_p * max(1, R))(*send) if send is not None else None
+    rp = (ctypes.c_void_p * max(1, len(recv)))(*recv) if recv is not None else None
+    o = _options(**opts)
+    dt = DTYPES.get(dtype, dtype if isinstance(dtype, int) else 99)
+    opc = OPS.get(op, op if isinstance(op, int) else 99)
+    if kind == "allreduce":
+        return _allreduce_ring_staged(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
+    if kind == "reduce_scatter":
+        return _reduce_scatter(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
+    return _all_gather(sp, rp, R, n, dt, nslices, ctypes.byref(o), stream)
 
 
 def allreduce_ring_ptrs(ptrs, count: int, dtype: str, op: str = "sum", nslices: int = 1,

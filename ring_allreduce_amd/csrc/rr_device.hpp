@@ -1,6 +1,7 @@
 // rr_device.hpp -- device-side building blocks of the ring kernels (gfx950).
 //
-//  * element folds for int32 / fp32 / bf16, SUM and MAX, on 16-byte vectors;
+//  * element folds for int32 / fp32 / bf16 / fp16, SUM, MAX, MIN and PROD, on
+//    16-byte vectors;
 //  * the counting-signal layer: 64-bit agent-scope counters in HBM, waiters
 //    holding a private shadow, rolling comparison, bounded waits.
 //
@@ -20,14 +21,19 @@ namespace rr {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
-enum : int { OP_SUM = 0, OP_MAX = 1 };
+enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2, DT_F16 = 3 };
+enum : int { OP_SUM = 0, OP_MAX = 1, OP_MIN = 2, OP_PROD = 3 };
 enum : int { SYNC_NONE = 0, SYNC_P2P = 1, SYNC_BARRIER = 2, SYNC_PER_PEER = 3 };
 
-template <int DT> struct ElemBytes { static constexpr int value = DT == DT_BF16 ? 2 : 4; };
+template <int DT> struct ElemBytes {
+    static constexpr int value = DT == DT_BF16 || DT == DT_F16 ? 2 : 4;
+};
 
 // ------------------------------------------------------------------ folds --
 // fold(in, local): the receiver's new value, `in` being the incoming partial.
+// SUM and PROD: one operation, rounded to the storage format (int32 wraps).
+// MAX (MIN): the local value if it compares greater (less), else the incoming
+// one -- a selection, no arithmetic.
 
 // Round a binary32 value to the nearest bfloat16, ties to even; any NaN becomes
 // the quiet NaN 0x7FC0.  Adding 0x7FFF plus the lowest kept bit and truncating
@@ -39,48 +45,73 @@ __device__ __forceinline__ uint32_t bf16_round(float f) {
     return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0x7FC0u : r;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+// The 16-bit formats, two to a 32-bit lane (the lower address in the low half).
+// A bf16 or fp16 SUM or PROD is computed in binary32 and rounded once to the
+// format: equal to the correctly rounded operation, because binary32 holds the
+// exact product of two such values (fp16) or enough of it that no false tie
+// arises (bf16: at most 16 significant bits), and because 24 >= 2p + 2 for the
+// sums (p = 8, 11).
+template <int DT> struct Codec;
+template <> struct Codec<DT_BF16> {
+    __device__ static float lo(uint32_t p) { return __uint_as_float(p << 16); }
+    __device__ static float hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+    __device__ static uint32_t round(float f) { return bf16_round(f); }
+};
+template <> struct Codec<DT_F16> {
+    __device__ static float lo(uint32_t p) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+    }
+    __device__ static float hi(uint32_t p) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+    }
+    // round to nearest even (the default mode of the conversion); NaN -> 0x7E00.
+    // The empty asm keeps the binary32 result as it is: without it the compiler
+    // folds "multiply, then convert" into one mixed-precision fma with a +0
+    // addend, which turns a -0 product into +0.
+    __device__ static uint32_t round(float f) {
+        asm volatile("" : "+v"(f));
+        return f != f ? 0x7E00u : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+    }
+};
 
-template <int DT, int OP> struct Fold;
+template <int OP> __device__ __forceinline__ float arith(float in, float lo) {
+    return OP == OP_PROD ? in * lo : in + lo;
+}
+template <int OP, typename T> __device__ __forceinline__ bool local_wins(T in, T lo) {
+    return OP == OP_MAX ? lo > in : lo < in;
+}
 
-template <> struct Fold<DT_I32, OP_SUM> {
-    __device__ static uint32_t lane(uint32_t in, uint32_t lo) { return in + lo; }  // wraps
-};
-template <> struct Fold<DT_I32, OP_MAX> {
-    __device__ static uint32_t lane(uint32_t in, uint32_t lo) {
-        return (int32_t)lo > (int32_t)in ? lo : in;
-    }
-};
-template <> struct Fold<DT_F32, OP_SUM> {
-    __device__ static uint32_t lane(uint32_t in, uint32_t lo) {
-        return __float_as_uint(__uint_as_float(in) + __uint_as_float(lo));
-    }
-};
-template <> struct Fold<DT_F32, OP_MAX> {
-    __device__ static uint32_t lane(uint32_t in, uint32_t lo) {
-        return __uint_as_float(lo) > __uint_as_float(in) ? lo : in;
-    }
-};
-// bf16: a 32-bit lane carries two elements, the lower address in the low half.
-template <> struct Fold<DT_BF16, OP_SUM> {
-    __device__ static uint32_t half(uint32_t in, uint32_t lo) {  // operands in the low 16 bits
-        return bf16_round(bf16_lo(in) + bf16_lo(lo));
-    }
-    __device__ static uint32_t lane(uint32_t in, uint32_t lo) {
-        const uint32_t a = bf16_round(bf16_lo(in) + bf16_lo(lo));
-        const uint32_t b = bf16_round(bf16_hi(in) + bf16_hi(lo));
-        return a | (b << 16);
-    }
-};
-template <> struct Fold<DT_BF16, OP_MAX> {
+template <int DT, int OP> struct Fold {
+    static constexpr bool kArith = OP == OP_SUM || OP == OP_PROD;
+
+    // One 16-bit element, operands in the low 16 bits.
     __device__ static uint32_t half(uint32_t in, uint32_t lo) {
-        return bf16_lo(lo) > bf16_lo(in) ? (lo & 0xFFFFu) : (in & 0xFFFFu);
+        const float a = Codec<DT>::lo(in), b = Codec<DT>::lo(lo);
+        if constexpr (kArith) return Codec<DT>::round(arith<OP>(a, b));
+        return local_wins<OP>(a, b) ? (lo & 0xFFFFu) : (in & 0xFFFFu);
     }
+
+    // One 32-bit lane: one int32 / fp32 element or two 16-bit elements.
     __device__ static uint32_t lane(uint32_t in, uint32_t lo) {
-        const uint32_t a = bf16_lo(lo) > bf16_lo(in) ? lo : in;
-        const uint32_t b = bf16_hi(lo) > bf16_hi(in) ? lo : in;
-        return (a & 0xFFFFu) | (b & 0xFFFF0000u);
+        if constexpr (DT == DT_I32) {
+            if constexpr (OP == OP_SUM) return in + lo;   // wraps
+            if constexpr (OP == OP_PROD) return in * lo;  // low 32 bits: wraps
+            return local_wins<OP>((int32_t)in, (int32_t)lo) ? lo : in;
+        } else if constexpr (DT == DT_F32) {
+            const float a = __uint_as_float(in), b = __uint_as_float(lo);
+            if constexpr (kArith) return __float_as_uint(arith<OP>(a, b));
+            return local_wins<OP>(a, b) ? lo : in;
+        } else {
+            const float al = Codec<DT>::lo(in), bl = Codec<DT>::lo(lo);
+            const float ah = Codec<DT>::hi(in), bh = Codec<DT>::hi(lo);
+            if constexpr (kArith) {
+                return Codec<DT>::round(arith<OP>(al, bl)) |
+                       (Codec<DT>::round(arith<OP>(ah, bh)) << 16);
+            }
+            const uint32_t l = local_wins<OP>(al, bl) ? lo : in;
+            const uint32_t h = local_wins<OP>(ah, bh) ? lo : in;
+            return (l & 0xFFFFu) | (h & 0xFFFF0000u);
+        }
     }
 };
 
@@ -97,7 +128,7 @@ __device__ __forceinline__ u32x4 fold4(u32x4 in, u32x4 lo) {
 // One element at a time, for the ragged end of the last chunk.
 template <int DT, int OP>
 __device__ __forceinline__ void fold_one(const void* in, void* lo) {
-    if constexpr (DT == DT_BF16) {
+    if constexpr (ElemBytes<DT>::value == 2) {
         const uint16_t a = *(const uint16_t*)in;
         uint16_t* b = (uint16_t*)lo;
         *b = (uint16_t)Fold<DT, OP>::half(a, *b);

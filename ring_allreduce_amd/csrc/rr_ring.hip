@@ -425,6 +425,286 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
     }
 }
 
+// ------------------------------------------------------ the staged loop --
+//
+// The ring as the primitives of one rank (the loosp.cn post, sections 8-10;
+// Table V of the paper it discusses), out of place.  Each rank owns a receive
+// buffer of kFifoSlots chunk-sized slots per lane; at step k a rank reads the
+// message of step k-1 from its own slot (k-1) mod kFifoSlots, combines it with
+// its input and/or writes its output, and sends the result into its
+// successor's slot k mod kFifoSlots.  Two counting signals per (lane, rank)
+// hand the steps off: `ready` (the predecessor's message has landed; one
+// arrival per step) and `credit` (the successor has consumed a message, so its
+// slot may be written again; one arrival per message).  A sender needs credit
+// for message k - kFifoSlots before it writes message k.
+//
+//   AllReduce       steps 0..2R-2: send, recvReduceSend x (R-2),
+//                   recvReduceCopySend, recvCopySend x (R-2), recv; rank r
+//                   handles chunk (r - k) mod R at step k.
+//   ReduceScatter   the standalone numbering (rank r keeps block r): steps
+//                   0..R-1, send, recvReduceSend x (R-2), recvReduceCopy; chunk
+//                   (r - k - 1) mod R.
+//   AllGather       steps 0..R-1, copySend, recvCopySend x (R-2), recv; chunk
+//                   (r - k) mod R.
+constexpr int kFifoSlots = 2;
+constexpr int kStagedBlock = 512;
+enum : int { MODE_ALLREDUCE = 0, MODE_RS = 1, MODE_AG = 2 };
+enum : int { P_SEND = 0, P_RRS = 1, P_RRCS = 2, P_RCS = 3, P_RECV = 4, P_RRC = 5, P_CS = 6 };
+
+template <int P> struct Prim {
+    static constexpr bool in = P != P_SEND && P != P_CS;  // reads the receive slot
+    static constexpr bool local = P == P_SEND || P == P_RRS || P == P_RRCS || P == P_RRC || P == P_CS;
+    static constexpr bool reduce = P == P_RRS || P == P_RRCS || P == P_RRC;
+    static constexpr bool out = P != P_SEND && P != P_RRS;  // writes the output
+    static constexpr bool send = P != P_RECV && P != P_RRC;  // writes the successor's slot
+};
+
+struct StagedArgs {
+    const void* send[kMaxDevices];
+    void* recv[kMaxDevices];
+    char* fifo;            // R ranks x kFifoSlots slots x slot_len elements
+    uint64_t slot_len;     // elements per slot (chunk_len rounded up to a vector)
+    uint64_t n;            // AllReduce: elements per rank; else elements per block
+    uint64_t chunk_len;    // AllReduce: the partition's chunk length; else n
+    uint64_t slice_len;
+    uint64_t sub_len;
+    uint64_t* ready;
+    uint64_t* ready_shadow;
+    uint64_t* credit;
+    uint64_t* credit_shadow;
+    uint64_t* xcc_table;
+    ErrorRecord* err;
+    uint64_t timeout_ticks;
+    uint32_t generation;
+    uint32_t inject;
+    int32_t R;
+    int32_t team;
+    int32_t cols;          // lanes = workgroups per rank
+    int32_t mode;
+    int32_t k_first;       // steps this launch runs
+    int32_t k_last;
+    int32_t xcd_map;
+    int32_t aligned;       // every operand 16-byte aligned: the vector path
+};
+
+// One step's data over n elements: in (the receive slot, device-scope loads),
+// local (the rank's input), out (its output), next (the successor's slot).
+template <int DT, int OP, int BLOCK, int P>
+__device__ __forceinline__ void staged_piece(const void* in, const void* local, void* out,
+                                             void* next, uint64_t n, bool aligned) {
+    using Q = Prim<P>;
+    constexpr int ES = ElemBytes<DT>::value;
+    constexpr int V = 16 / ES;
+    constexpr int U = 4;
+    // (a descriptor of zero bytes when the primitive reads no slot; never used)
+    const __amdgpu_buffer_rsrc_t rs = incoming(in, Q::in ? n * ES : 0);
+    uint64_t done = 0;
+    if (aligned) {
+        const uint32_t nv = (uint32_t)(n / V);
+        const u32x4* __restrict__ lp = (const u32x4*)local;
+        u32x4* __restrict__ op = (u32x4*)out;
+        u32x4* __restrict__ np = (u32x4*)next;
+        uint32_t i = threadIdx.x;
+        for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
+            u32x4 x[U], y[U];
+            if constexpr (Q::in) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
+            }
+            if constexpr (Q::local) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) y[u] = lp[i + u * BLOCK];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                u32x4 v;
+                if constexpr (Q::reduce) v = fold4<DT, OP>(x[u], y[u]);
+                else if constexpr (Q::in) v = x[u];
+                else v = y[u];
+                if constexpr (Q::out) op[i + u * BLOCK] = v;
+                if constexpr (Q::send) np[i + u * BLOCK] = v;
+            }
+        }
+        for (; i < nv; i += BLOCK) {
+            u32x4 v;
+            if constexpr (Q::reduce) v = fold4<DT, OP>(load_in(rs, i), lp[i]);
+            else if constexpr (Q::in) v = load_in(rs, i);
+            else v = lp[i];
+            if constexpr (Q::out) op[i] = v;
+            if constexpr (Q::send) np[i] = v;
+        }
+        done = (uint64_t)nv * V;
+    }
+    // element by element: the ragged end, or everything when an operand is not
+    // 16-byte aligned
+    for (uint64_t t = done + threadIdx.x; t < n; t += BLOCK) {
+        const int off = (int)(t * ES);
+        if constexpr (ES == 2) {
+            uint16_t x = 0, y = 0, v;
+            if constexpr (Q::in) x = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kAuxDeviceScope);
+            if constexpr (Q::local) y = ((const uint16_t*)local)[t];
+            if constexpr (Q::reduce) v = (uint16_t)Fold<DT, OP>::half(x, y);
+            else v = Q::in ? x : y;
+            if constexpr (Q::out) ((uint16_t*)out)[t] = v;
+            if constexpr (Q::send) ((uint16_t*)next)[t] = v;
+        } else {
+            uint32_t x = 0, y = 0, v;
+            if constexpr (Q::in) x = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kAuxDeviceScope);
+            if constexpr (Q::local) y = ((const uint32_t*)local)[t];
+            if constexpr (Q::reduce) v = Fold<DT, OP>::lane(x, y);
+            else v = Q::in ? x : y;
+            if constexpr (Q::out) ((uint32_t*)out)[t] = v;
+            if constexpr (Q::send) ((uint32_t*)next)[t] = v;
+        }
+    }
+}
+
+// A piece longer than one buffer descriptor can cover is moved in parts.
+template <int DT, int OP, int BLOCK, int P>
+__device__ __forceinline__ void staged_move(const char* in, const char* local, char* out, char* next,
+                                            uint64_t n, bool aligned) {
+    constexpr int ES = ElemBytes<DT>::value;
+    constexpr uint64_t kPart = kPieceBytes / ES;
+    for (uint64_t p = 0; p < n; p += kPart) {
+        const uint64_t m = umin(kPart, n - p);
+        staged_piece<DT, OP, BLOCK, P>(in + p * ES, local + p * ES, out + p * ES, next + p * ES, m,
+                                       aligned);
+    }
+}
+
+template <int DT, int OP, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
+    constexpr int ES = ElemBytes<DT>::value;
+    const int R = a.R;
+    const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
+    const int r = pl.rank, lane = pl.col;
+    if (lane >= a.cols) return;  // padding column
+    const int succ = r + 1 == R ? 0 : r + 1;
+    const int pred = r == 0 ? R - 1 : r - 1;
+    const bool synced = a.k_last > a.k_first;
+    const int K = a.mode == MODE_ALLREDUCE ? 2 * R - 2 : R - 1;  // last step; steps < K send
+
+    __shared__ int s_stop;
+    __shared__ int s_local;
+    const uint32_t my_xcc = xcc_id() & 0xFu;
+    if (threadIdx.x == 0) {
+        s_stop = sig_read(&a.err->flag) != 0;  // a recorded failure is sticky
+        if (synced) publish_xcc(a.xcc_table, a.generation, my_xcc);
+    }
+    __syncthreads();
+    if (s_stop) return;
+
+    const int j = lane / a.team, w = lane - j * a.team;
+    const uint64_t off_lo = (uint64_t)j * a.slice_len + (uint64_t)w * a.sub_len;
+    const uint64_t off_hi =
+        umin(off_lo + a.sub_len, umin((uint64_t)(j + 1) * a.slice_len, a.chunk_len));
+    const int my_slot = lane * R + r;
+    const bool injected = r == 0 && lane == 0;
+    uint64_t ready_shadow = 0, credit_base = 0;
+    if (synced && threadIdx.x == 0) {
+        ready_shadow = a.ready_shadow[my_slot];
+        credit_base = a.credit_shadow[my_slot];
+    }
+    uint64_t credit_target = credit_base;
+    bool local = false, decided = false;
+
+    for (int k = a.k_first; k <= a.k_last; ++k) {
+        const bool has_in = k >= 1, has_send = k < K;
+        if (synced) {
+            if (threadIdx.x == 0) {
+                int stop = 0;
+                if (has_in) {  // the predecessor's message of step k-1
+                    uint64_t target = ready_shadow + 1;
+                    if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected && k == 1) target += 1;
+                    const WaitResult res = sig_wait(&a.ready[(uint64_t)my_slot * kSignalStride],
+                                                    target, a.err, a.timeout_ticks);
+                    if (res.status == WAIT_TIMEOUT)
+                        record_timeout(a.err, lane, r, k, target, res.observed);
+                    ready_shadow = target;
+                    stop = res.status != WAIT_OK;
+                }
+                if (!stop && has_send && k >= kFifoSlots) {  // the successor freed the slot
+                    credit_target += 1;
+                    const WaitResult res = sig_wait(&a.credit[(uint64_t)my_slot * kSignalStride],
+                                                    credit_target, a.err, a.timeout_ticks);
+                    if (res.status == WAIT_TIMEOUT)
+                        record_timeout(a.err, lane, r, k, credit_target, res.observed, succ);
+                    stop = res.status != WAIT_OK;
+                }
+                if (!stop && has_in) acquire_stores(local);
+                s_stop = stop;
+            }
+            __syncthreads();
+            if (s_stop) return;
+        }
+
+        const int c = wrap(r - k - (a.mode == MODE_RS ? 1 : 0), R);
+        const uint64_t base = a.mode == MODE_ALLREDUCE ? (uint64_t)c * a.chunk_len : 0;
+        const uint64_t len = a.mode == MODE_ALLREDUCE
+                                 ? (base < a.n ? umin(a.chunk_len, a.n - base) : 0)
+                                 : a.n;
+        const uint64_t lo = off_lo, hi = umin(off_hi, len);
+        if (lo < hi) {
+            const char* in = a.fifo + ((uint64_t)(r * kFifoSlots + (k + kFifoSlots - 1) % kFifoSlots) *
+                                           a.slot_len + lo) * ES;
+            char* next = a.fifo + ((uint64_t)(succ * kFifoSlots + k % kFifoSlots) * a.slot_len + lo) * ES;
+            const uint64_t lbase = a.mode == MODE_AG ? 0 : (uint64_t)c * a.chunk_len;
+            const uint64_t obase = a.mode == MODE_RS ? 0 : (uint64_t)c * a.chunk_len;
+            const char* lp = (const char*)a.send[r] + (lbase + lo) * ES;
+            char* op = (char*)a.recv[r] + (obase + lo) * ES;
+            const uint64_t m = hi - lo;
+            const bool al = a.aligned != 0;
+            if (a.mode == MODE_ALLREDUCE) {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_SEND>(in, lp, op, next, m, al);
+                else if (k < R - 1) staged_move<DT, OP, BLOCK, P_RRS>(in, lp, op, next, m, al);
+                else if (k == R - 1) staged_move<DT, OP, BLOCK, P_RRCS>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RCS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RECV>(in, lp, op, next, m, al);
+            } else if (a.mode == MODE_RS) {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_SEND>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RRS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RRC>(in, lp, op, next, m, al);
+            } else {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_CS>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RCS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RECV>(in, lp, op, next, m, al);
+            }
+        }
+
+        if (synced) {
+            if (!decided) {
+                if (threadIdx.x < 64) {
+                    const int v = column_on_one_xcd(a.xcc_table, a.generation, R, lane,
+                                                    a.xcd_map != 0, my_xcc, a.err, a.timeout_ticks);
+                    if (threadIdx.x == 0) {
+                        if (v < 0) record_timeout(a.err, lane, r, 0, a.generation, 0);
+                        s_local = v;
+                    }
+                }
+                __syncthreads();
+                if (s_local < 0) return;
+                local = s_local == 1;
+                decided = true;
+            }
+            // loads of the slot done and stores of the message visible, then both
+            // hand-offs
+            release_stores(local);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const bool drop = (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && k == 0;
+                if (has_send && !drop)
+                    sig_add(&a.ready[(uint64_t)(lane * R + succ) * kSignalStride], 1);
+                if (has_in) sig_add(&a.credit[(uint64_t)(lane * R + pred) * kSignalStride], 1);
+            }
+        }
+    }
+    if (synced && threadIdx.x == 0) {
+        a.ready_shadow[my_slot] = ready_shadow;
+        // every message this rank sends (K of them) is consumed and credited
+        a.credit_shadow[my_slot] = credit_base + (uint64_t)K;
+    }
+}
+
 // ---------------------------------------------------------- barrier only --
 
 struct BarrierArgs {
@@ -656,6 +936,10 @@ struct DeviceState {
     uint64_t* shadow = nullptr;
     uint64_t* xcc_table = nullptr;
     ErrorRecord* err = nullptr;
+    uint64_t* credit = nullptr;         // staged loop: slot-free signals, one per cache line
+    uint64_t* credit_shadow = nullptr;
+    char* fifo = nullptr;               // staged loop: receive buffers, grown on demand
+    size_t fifo_bytes = 0;
     uint32_t generation = 0;
 };
 
@@ -682,7 +966,7 @@ struct Plan {
 static inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 static inline uint64_t round_up(uint64_t a, uint64_t b) { return ceil_div(a, b) * b; }
 
-static size_t elem_bytes(int dt) { return dt == RR_BF16 ? 2 : 4; }
+static size_t elem_bytes(int dt) { return dt == RR_BF16 || dt == RR_FP16 ? 2 : 4; }
 
 static bool hip_ok(hipError_t e) { return e == hipSuccess; }
 
@@ -698,8 +982,10 @@ static rr_status_t ensure_device(DeviceState** out) {
         if (!hip_ok(hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev)) ||
             d.wall_khz <= 0)
             d.wall_khz = 100000;  // the gfx9 constant-rate clock runs at 100 MHz
-        // signals (one per cache line), shadows, the XCC table, the error record
-        const size_t words = (size_t)kSlots * kSignalStride + 2 * (size_t)kSlots + 16;
+        // signals (one per cache line), shadows, the XCC table, the error record,
+        // then the staged loop's credit signals and their shadows
+        const size_t words = 2 * ((size_t)kSlots * kSignalStride + (size_t)kSlots) +
+                             (size_t)kSlots + 16;
         void* p = nullptr;
         if (!hip_ok(hipMalloc(&p, words * sizeof(uint64_t)))) return RR_ERR_NOMEM;
         if (!hip_ok(hipMemset(p, 0, words * sizeof(uint64_t)))) {
@@ -711,6 +997,8 @@ static rr_status_t ensure_device(DeviceState** out) {
         d.shadow = d.mem + (size_t)kSlots * kSignalStride;
         d.xcc_table = d.shadow + kSlots;
         d.err = (ErrorRecord*)(d.xcc_table + kSlots);
+        d.credit = d.xcc_table + kSlots + 16;
+        d.credit_shadow = d.credit + (size_t)kSlots * kSignalStride;
         d.ready = true;
     }
     *out = &d;
@@ -734,22 +1022,61 @@ static RingKernel ring_kernel_for_block(int block) {
     }
 }
 
-static RingKernel pick_ring_kernel(int dt, int op, int block) {
-    if (dt == RR_INT32) return op == RR_SUM ? ring_kernel_for_block<DT_I32, OP_SUM>(block)
-                                             : ring_kernel_for_block<DT_I32, OP_MAX>(block);
-    if (dt == RR_FP32) return op == RR_SUM ? ring_kernel_for_block<DT_F32, OP_SUM>(block)
-                                            : ring_kernel_for_block<DT_F32, OP_MAX>(block);
-    return op == RR_SUM ? ring_kernel_for_block<DT_BF16, OP_SUM>(block)
-                        : ring_kernel_for_block<DT_BF16, OP_MAX>(block);
+template <int DT>
+static RingKernel ring_kernel_for_op(int op, int block) {
+    switch (op) {
+        case RR_SUM: return ring_kernel_for_block<DT, OP_SUM>(block);
+        case RR_MAX: return ring_kernel_for_block<DT, OP_MAX>(block);
+        case RR_MIN: return ring_kernel_for_block<DT, OP_MIN>(block);
+        case RR_PROD: return ring_kernel_for_block<DT, OP_PROD>(block);
+        default: return nullptr;
+    }
 }
+
+static RingKernel pick_ring_kernel(int dt, int op, int block) {
+    switch (dt) {
+        case RR_INT32: return ring_kernel_for_op<DT_I32>(op, block);
+        case RR_FP32: return ring_kernel_for_op<DT_F32>(op, block);
+        case RR_BF16: return ring_kernel_for_op<DT_BF16>(op, block);
+        case RR_FP16: return ring_kernel_for_op<DT_F16>(op, block);
+        default: return nullptr;
+    }
+}
+
+typedef void (*StagedKernel)(StagedArgs);
+
+template <int DT>
+static StagedKernel staged_kernel_for_op(int op) {
+    switch (op) {
+        case RR_SUM: return staged_kernel<DT, OP_SUM, kStagedBlock>;
+        case RR_MAX: return staged_kernel<DT, OP_MAX, kStagedBlock>;
+        case RR_MIN: return staged_kernel<DT, OP_MIN, kStagedBlock>;
+        case RR_PROD: return staged_kernel<DT, OP_PROD, kStagedBlock>;
+        default: return nullptr;
+    }
+}
+
+static StagedKernel pick_staged_kernel(int dt, int op) {
+    switch (dt) {
+        case RR_INT32: return staged_kernel_for_op<DT_I32>(op);
+        case RR_FP32: return staged_kernel_for_op<DT_F32>(op);
+        case RR_BF16: return staged_kernel_for_op<DT_BF16>(op);
+        case RR_FP16: return staged_kernel_for_op<DT_F16>(op);
+        default: return nullptr;
+    }
+}
+
+static bool valid_dtype(int dt) {
+    return dt == RR_INT32 || dt == RR_FP32 || dt == RR_BF16 || dt == RR_FP16;
+}
+static bool valid_op(int op) { return op == RR_SUM || op == RR_MAX || op == RR_MIN || op == RR_PROD; }
 
 // Argument checks that need no device.
 static rr_status_t check_args(void* const* bufs, int R, size_t count, int dt, int op, int nslices,
                               const rr_options_t* opt) {
     if (R < 1 || R > RR_MAX_RANKS) return RR_ERR_INVALID;
     if (nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
-    if (dt != RR_INT32 && dt != RR_FP32 && dt != RR_BF16) return RR_ERR_INVALID;
-    if (op != RR_SUM && op != RR_MAX) return RR_ERR_INVALID;
+    if (!valid_dtype(dt) || !valid_op(op)) return RR_ERR_INVALID;
     if (count > (size_t)1 << 40) return RR_ERR_INVALID;
     if (opt) {
         if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
@@ -990,6 +1317,192 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     return RR_OK;
 }
 
+// ------------------------------------------------------ the staged loop, host
+
+static int staged_last_step(int R, int mode) { return mode == MODE_ALLREDUCE ? 2 * R - 2 : R - 1; }
+
+// n: AllReduce elements per rank; ReduceScatter / AllGather elements per block.
+static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int dt, int op,
+                                    int nslices, int mode, const rr_options_t* opt, Plan* p) {
+    const uint64_t es = elem_bytes(dt);
+    const uint64_t V = 16 / es;
+    const int requested = opt ? opt->sync : RR_SYNC_AUTO;
+    const uint32_t flags = opt ? opt->flags : 0;
+    if (opt && opt->block != 0 && opt->block != kStagedBlock) return RR_ERR_UNSUPPORTED;
+    if (requested == RR_SYNC_BARRIER) return RR_ERR_UNSUPPORTED;  // credits pace the loop
+    p->block = kStagedBlock;
+    p->fuse = 0;
+    p->chunk_len = mode == MODE_ALLREDUCE ? round_up(ceil_div(n, (uint64_t)R), V) : n;
+    p->slice_len = round_up(ceil_div(p->chunk_len, (uint64_t)nslices), V);
+    p->g_first = 0;
+    p->g_last = staged_last_step(R, mode);
+    p->hbm_bytes = R < 2 ? 0
+                   : mode == MODE_ALLREDUCE ? (6ull * R - 4) * n * es
+                                            : (3ull * R - 1) * (uint64_t)R * n * es;
+    const void* kernel = (const void*)pick_staged_kernel(dt, mode == MODE_AG ? RR_SUM : op);
+    if (!kernel) return RR_ERR_INVALID;
+    p->resident_max = resident_limit(d, kernel, kStagedBlock);
+    const int target_cols = std::max(1, d->cus * 16 * 64 / kStagedBlock / R);
+    int team;
+    if (opt && opt->team > 0) {
+        team = opt->team;
+    } else {
+        const uint64_t by_size = std::max<uint64_t>(1, p->slice_len / V / ((uint64_t)kStagedBlock * 4));
+        const uint64_t wanted = ceil_div((uint64_t)target_cols, (uint64_t)nslices);
+        team = (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
+    }
+    const int max_team = std::max(1, kSlots / (R * nslices));
+    if (team > max_team) {
+        if (opt && opt->team > 0) return RR_ERR_UNSUPPORTED;
+        team = max_team;
+    }
+    p->team = team;
+    p->depth = 1;
+    p->rounds = 1;
+    p->cols = nslices * team;
+    p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
+    p->xcd_map = (flags & RR_FLAG_NO_XCD_MAP) ? 0 : 1;
+    const uint64_t cols_launched = p->xcd_map ? round_up((uint64_t)p->cols, 8) : p->cols;
+    if ((uint64_t)R * cols_launched > (1ull << 30)) return RR_ERR_INVALID;
+    p->grid = (int)(R * cols_launched);
+    int sync = requested;
+    if (sync == RR_SYNC_AUTO) sync = p->grid <= p->resident_max ? RR_SYNC_P2P : RR_SYNC_LAUNCH;
+    if (sync == RR_SYNC_P2P && (p->grid > p->resident_max || p->grid > kSlots))
+        return RR_ERR_UNSUPPORTED;
+    p->sync = sync;
+    p->launches = sync == RR_SYNC_LAUNCH ? p->g_last + 1 : 1;
+    p->coop = 0;
+    return RR_OK;
+}
+
+// Send and receive buffers: non-null, 16-byte aligned, pairwise disjoint,
+// except that an AllReduce may receive in place (recv[r] == send[r]).
+static rr_status_t check_staged_args(const void* const* send, void* const* recv, int R, uint64_t n,
+                                     int dt, int op, int nslices, int mode, const rr_options_t* opt) {
+    if (R < 1 || R > RR_MAX_RANKS || nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
+    if (!valid_dtype(dt) || !valid_op(op)) return RR_ERR_INVALID;
+    if (n > (uint64_t)1 << 40 || (uint64_t)R * n > (uint64_t)1 << 40) return RR_ERR_INVALID;
+    if (opt) {
+        if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
+        if (opt->team < 0 || opt->team > 4096) return RR_ERR_INVALID;
+        if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
+            return RR_ERR_INVALID;
+    }
+    if (!send || !recv) return RR_ERR_INVALID;
+    if (n == 0) return RR_OK;
+    const uint64_t es = elem_bytes(dt);
+    const uint64_t sbytes = (mode == MODE_RS ? (uint64_t)R : 1) * n * es;
+    const uint64_t rbytes = (mode == MODE_AG ? (uint64_t)R : 1) * n * es;
+    std::vector<std::pair<uintptr_t, uint64_t>> iv;
+    for (int r = 0; r < R; ++r) {
+        if (!send[r] || !recv[r]) return RR_ERR_INVALID;
+        if ((uintptr_t)send[r] % 16 || (uintptr_t)recv[r] % 16) return RR_ERR_INVALID;
+        iv.push_back({(uintptr_t)send[r], sbytes});
+        const bool in_place = mode == MODE_ALLREDUCE && (const void*)recv[r] == send[r];
+        if (!in_place) iv.push_back({(uintptr_t)recv[r], rbytes});
+    }
+    std::sort(iv.begin(), iv.end());
+    for (size_t i = 0; i + 1 < iv.size(); ++i)
+        if (iv[i].first + iv[i].second > iv[i + 1].first) return RR_ERR_INVALID;
+    return RR_OK;
+}
+
+static rr_status_t ensure_fifo(DeviceState* d, size_t bytes) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (d->fifo_bytes >= bytes) return RR_OK;
+    if (d->fifo) {
+        if (!hip_ok(hipDeviceSynchronize())) return RR_ERR_HIP;
+        (void)hipFree(d->fifo);
+        d->fifo = nullptr;
+        d->fifo_bytes = 0;
+    }
+    void* p = nullptr;
+    if (!hip_ok(hipMalloc(&p, bytes))) return RR_ERR_NOMEM;
+    d->fifo = (char*)p;
+    d->fifo_bytes = bytes;
+    return RR_OK;
+}
+
+static rr_status_t copy_bytes(void* dst, const void* src, uint64_t bytes, const DeviceState* d,
+                              hipStream_t s) {
+    const uint64_t nvec = bytes / 16;
+    const uint32_t ntail = (uint32_t)(bytes % 16);
+    const unsigned grid = (unsigned)std::max<uint64_t>(
+        1, std::min<uint64_t>((uint64_t)d->cus * 16, ceil_div(nvec, 2048)));
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst,
+                       nvec, (const uint8_t*)src + nvec * 16, (uint8_t*)dst + nvec * 16, ntail);
+    return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
+}
+
+static rr_status_t run_staged(const void* const* send, void* const* recv, int R, uint64_t n, int dt,
+                              int op, int nslices, int mode, const rr_options_t* opt,
+                              rr_stream_t stream) {
+    rr_status_t st = check_staged_args(send, recv, R, n, dt, op, nslices, mode, opt);
+    if (st != RR_OK || n == 0) return st;
+    DeviceState* d = nullptr;
+    if ((st = ensure_device(&d)) != RR_OK) return st;
+    const uint64_t es = elem_bytes(dt);
+    const uint64_t sbytes = (mode == MODE_RS ? (uint64_t)R : 1) * n * es;
+    const uint64_t rbytes = (mode == MODE_AG ? (uint64_t)R : 1) * n * es;
+    if (!(opt && (opt->flags & RR_FLAG_NO_POINTER_CHECK))) {
+        if ((st = check_extents((void* const*)send, R, sbytes)) != RR_OK) return st;
+        if ((st = check_extents(recv, R, rbytes)) != RR_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (R == 1) {  // nothing to exchange: the output is the input
+        if ((const void*)recv[0] == send[0]) return RR_OK;
+        return copy_bytes(recv[0], send[0], n * es, d, s);
+    }
+    Plan p;
+    if ((st = make_staged_plan(d, R, n, dt, op, nslices, mode, opt, &p)) != RR_OK) return st;
+    const uint64_t slot_len = round_up(p.chunk_len, 16 / es);
+    if ((st = ensure_fifo(d, (size_t)R * kFifoSlots * slot_len * es)) != RR_OK) return st;
+
+    StagedArgs a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < R; ++r) {
+        a.send[r] = send[r];
+        a.recv[r] = recv[r];
+    }
+    a.fifo = d->fifo;
+    a.slot_len = slot_len;
+    a.n = n;
+    a.chunk_len = p.chunk_len;
+    a.slice_len = p.slice_len;
+    a.sub_len = p.sub_len;
+    a.ready = d->sig;
+    a.ready_shadow = d->shadow;
+    a.credit = d->credit;
+    a.credit_shadow = d->credit_shadow;
+    a.xcc_table = d->xcc_table;
+    a.err = d->err;
+    a.timeout_ticks = timeout_ticks(d, opt);
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (++d->generation == 0) d->generation = 1;
+        a.generation = d->generation;
+    }
+    a.inject = opt ? opt->inject : 0;
+    a.R = R;
+    a.team = p.team;
+    a.cols = p.cols;
+    a.mode = mode;
+    a.xcd_map = p.xcd_map;
+    a.aligned = mode == MODE_ALLREDUCE || (n * es) % 16 == 0;
+    StagedKernel k = pick_staged_kernel(dt, mode == MODE_AG ? RR_SUM : op);
+    if (p.sync == RR_SYNC_LAUNCH) {
+        for (int step = p.g_first; step <= p.g_last; ++step) {
+            a.k_first = a.k_last = step;
+            hipLaunchKernelGGL(k, dim3(p.grid), dim3(p.block), 0, s, a);
+        }
+    } else {
+        a.k_first = p.g_first;
+        a.k_last = p.g_last;
+        hipLaunchKernelGGL(k, dim3(p.grid), dim3(p.block), 0, s, a);
+    }
+    return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
+}
+
 static rr_status_t fill(uint64_t* p, uint64_t n, uint64_t value, uint64_t stride, hipStream_t s) {
     if (n == 0) return RR_OK;
     const unsigned grid = (unsigned)std::min<uint64_t>(1024, ceil_div(n, 256));
@@ -1048,16 +1561,37 @@ rr_status_t all_gather_ring(void* const* bufs, int R, size_t count, rr_dtype_t d
     return run_ring(bufs, R, count, dt, RR_SUM, nslices, 2, nullptr, stream);
 }
 
+rr_status_t allreduce_ring_staged(const void* const* sendbufs, void* const* recvbufs, int R,
+                                  size_t count, rr_dtype_t dt, rr_op_t op, int nslices,
+                                  const rr_options_t* opt, rr_stream_t stream) {
+    return run_staged(sendbufs, recvbufs, R, count, dt, op, nslices, MODE_ALLREDUCE, opt, stream);
+}
+
+rr_status_t reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int R,
+                           size_t recvcount, rr_dtype_t dt, rr_op_t op, int nslices,
+                           const rr_options_t* opt, rr_stream_t stream) {
+    return run_staged(sendbufs, recvbufs, R, recvcount, dt, op, nslices, MODE_RS, opt, stream);
+}
+
+rr_status_t all_gather(const void* const* sendbufs, void* const* recvbufs, int R, size_t sendcount,
+                       rr_dtype_t dt, int nslices, const rr_options_t* opt, rr_stream_t stream) {
+    return run_staged(sendbufs, recvbufs, R, sendcount, dt, RR_SUM, nslices, MODE_AG, opt, stream);
+}
+
 rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int phase,
                           const rr_options_t* opt, rr_plan_t* out) {
-    if (!out || phase < 0 || phase > 2) return RR_ERR_INVALID;
+    if (!out || phase < 0 || phase > 5) return RR_ERR_INVALID;
     if (R < 1 || R > RR_MAX_RANKS || nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
-    if (dt != RR_INT32 && dt != RR_FP32 && dt != RR_BF16) return RR_ERR_INVALID;
+    if (!valid_dtype(dt)) return RR_ERR_INVALID;
     DeviceState* d = nullptr;
     rr_status_t st = ensure_device(&d);
     if (st != RR_OK) return st;
     Plan p;
-    if ((st = make_plan(d, R, count, dt, RR_SUM, nslices, phase, opt, &p)) != RR_OK) return st;
+    if (phase <= 2)
+        st = make_plan(d, R, count, dt, RR_SUM, nslices, phase, opt, &p);
+    else
+        st = make_staged_plan(d, R, count, dt, RR_SUM, nslices, phase - 3, opt, &p);
+    if (st != RR_OK) return st;
     out->sync = p.sync;
     out->team = p.team;
     out->rounds = p.rounds;
@@ -1252,6 +1786,8 @@ rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {
     // clear the record and restore sig == shadow everywhere
     if ((st = fill(d->sig, kSlots, 0, kSignalStride, s)) != RR_OK) return st;
     if ((st = fill(d->shadow, kSlots, 0, 1, s)) != RR_OK) return st;
+    if ((st = fill(d->credit, kSlots, 0, kSignalStride, s)) != RR_OK) return st;
+    if ((st = fill(d->credit_shadow, kSlots, 0, 1, s)) != RR_OK) return st;
     if ((st = fill((uint64_t*)d->err, sizeof(ErrorRecord) / 8, 0, 1, s)) != RR_OK) return st;
     if (!hip_ok(hipStreamSynchronize(s))) return RR_ERR_HIP;
     return e.status == RR_ERR_TIMEOUT ? RR_ERR_TIMEOUT : RR_ERR_HIP;
@@ -1268,7 +1804,9 @@ rr_status_t rr_workspace_preset(uint64_t value, rr_stream_t stream) {
     if (st != RR_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if ((st = fill(d->sig, kSlots, value, kSignalStride, s)) != RR_OK) return st;
-    return fill(d->shadow, kSlots, value, 1, s);
+    if ((st = fill(d->shadow, kSlots, value, 1, s)) != RR_OK) return st;
+    if ((st = fill(d->credit, kSlots, value, kSignalStride, s)) != RR_OK) return st;
+    return fill(d->credit_shadow, kSlots, value, 1, s);
 }
 
 rr_status_t rr_hbm_copy(void* dst, const void* src, size_t bytes, rr_stream_t stream) {
@@ -1315,6 +1853,7 @@ void rr_finalize(void) {
         (void)hipSetDevice(i);
         (void)hipDeviceSynchronize();
         (void)hipFree(d.mem);
+        if (d.fifo) (void)hipFree(d.fifo);
         (void)hipSetDevice(prev);
         d = DeviceState();
     }

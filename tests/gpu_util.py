@@ -7,11 +7,13 @@ import torch
 
 import oracle
 
-TORCH = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16}
-RAW_NP = {"int32": np.uint32, "fp32": np.uint32, "bf16": np.uint16}
-RAW_TORCH = {"int32": torch.int32, "fp32": torch.int32, "bf16": torch.int16}
+TORCH = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16,
+         "fp16": torch.float16}
+RAW_NP = {"int32": np.uint32, "fp32": np.uint32, "bf16": np.uint16, "fp16": np.uint16}
+RAW_TORCH = {"int32": torch.int32, "fp32": torch.int32, "bf16": torch.int16, "fp16": torch.int16}
+SIGNED_NP = {"int32": np.int32, "fp32": np.int32, "bf16": np.int16, "fp16": np.int16}
 
-GUARD_FILL = {"int32": -0x5A5A5A5B, "fp32": -1.2345e-19, "bf16": -1.2345e-19}
+GUARD_FILL = {"int32": -0x5A5A5A5B, "fp32": -1.2345e-19, "bf16": -1.2345e-19, "fp16": -1.5e-5}
 
 
 def log(msg: str) -> None:
@@ -25,9 +27,15 @@ def to_slabs(rr, x, dtype, guard=True):
                           fill=GUARD_FILL[dtype] if guard else None)
     for r in range(R):
         slabs.ranks[r].view(RAW_TORCH[dtype]).copy_(
-            torch.from_numpy(x[r].view(RAW_NP[dtype]).view(
-                np.int32 if dtype != "bf16" else np.int16)))
+            torch.from_numpy(x[r].view(RAW_NP[dtype]).view(SIGNED_NP[dtype])))
     return slabs
+
+
+def to_device(a, dtype):
+    """One host array to a new device tensor, bit for bit."""
+    t = torch.empty(a.size, dtype=TORCH[dtype], device="cuda")
+    t.view(RAW_TORCH[dtype]).copy_(torch.from_numpy(a.view(RAW_NP[dtype]).view(SIGNED_NP[dtype])))
+    return t
 
 
 def to_host(t, dtype):

@@ -85,6 +85,45 @@ def test_invalid_arguments_rejected_on_host(rr, case):
     assert st == rr.RR_ERR_INVALID
 
 
+B = A + (1 << 30)  # a second region, far from the first
+
+
+@pytest.mark.parametrize("kind", ["allreduce", "reduce_scatter", "all_gather"])
+@pytest.mark.parametrize("case", [
+    dict(send=[], recv=[], n=16),                                              # R = 0
+    dict(send=[A + i * 4096 for i in range(65)], recv=[B + i * 4096 for i in range(65)], n=16),
+    dict(send=None, recv=[B, B + 4096], n=16),
+    dict(send=[A, A + 4096], recv=None, n=16),
+    dict(send=[A, 0], recv=[B, B + 4096], n=16),
+    dict(send=[A, A + 4096], recv=[B, B + 8], n=16),                           # misaligned
+    dict(send=[A, A + 32], recv=[B, B + 4096], n=16),                          # sends overlap
+    dict(send=[A, A + 4096], recv=[A + 4096 + 16, B], n=16),                   # recv overlaps a send
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, dtype=9),
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, op=9),
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, nslices=0),
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, sync=9),
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=(1 << 40) + 1),
+])
+def test_staged_invalid_arguments(rr, kind, case):
+    if kind == "all_gather" and "op" in case:
+        pytest.skip("all_gather takes no op")
+    kw = dict(case)
+    st = rr.staged_ptrs(kind, kw.pop("send"), kw.pop("recv"), kw.pop("n"), kw.pop("dtype", "fp32"),
+                        kw.pop("op", "sum"), kw.pop("nslices", 1), **kw)
+    assert st == rr.RR_ERR_INVALID
+
+
+def test_staged_in_place_rules(rr):
+    """An AllReduce may receive in place; the standalone collectives may not."""
+    assert rr.staged_ptrs("allreduce", [A, A + 4096], [A, A + 4096], 0, "fp32") == rr.RR_OK
+    same = [A, A + (1 << 20)]
+    assert rr.staged_ptrs("reduce_scatter", same, same, 16, "fp32") == rr.RR_ERR_INVALID
+    assert rr.staged_ptrs("all_gather", same, same, 16, "fp32") == rr.RR_ERR_INVALID
+    # a receive buffer may not be another rank's send buffer, even in an AllReduce
+    assert rr.staged_ptrs("allreduce", [A, A + 4096], [A + 4096, A], 16, "fp32") == \
+        rr.RR_ERR_INVALID
+
+
 def test_null_buffer_array(rr):
     st = rr._allreduce_ring(None, 4, 16, 1, 0, 1, None)
     assert st == rr.RR_ERR_INVALID
@@ -126,7 +165,8 @@ def test_copy_rejects_bad_arguments(rr):
 def test_plan_query_rejects_bad_arguments(rr):
     p = rr._Plan()
     assert rr._plan_query(0, 16, 1, 1, 0, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
-    assert rr._plan_query(4, 16, 1, 1, 3, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
+    assert rr._plan_query(4, 16, 1, 1, 6, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
+    assert rr._plan_query(4, 16, 4, 1, 0, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
     assert rr._plan_query(4, 16, 1, 1, 0, None, None) == rr.RR_ERR_INVALID
 
 
