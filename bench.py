@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--team", type=int, default=0)
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--path", default="ring",
+                    choices=["ring", "staged", "reduce_scatter", "all_gather"],
+                    help="ring: the in-place ring (headline); staged: the out-of-place staged "
+                         "primitives; reduce_scatter / all_gather: the standalone collectives "
+                         "over the same per-rank buffer (R blocks / one block per rank)")
     ap.add_argument("--fused", action="store_true",
                     help="fuse the last ReduceScatter hop with the first AllGather hop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,31 +130,65 @@ def main():
         w = w.with_(sync=args.sync)
     opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags,
                 fused=args.fused)
+    path = args.path
+    if path != "ring":
+        if w.sync == "barrier":
+            opts["sync"] = "auto"  # the staged loop is paced by its credits
+        opts.pop("fused")
+        if w.count % w.R:
+            print("the standalone collectives need a per-rank count divisible by R",
+                  file=sys.stderr)
+            return 2
+    blk = w.count // w.R
     rr.init()
-    p = rr.plan(w.R, w.count, w.dtype, w.nslices, **opts)
-    log(f"workload {w.name}: R={w.R} {w.dtype} {w.op} {w.bytes_per_rank / 2**20:.1f} MiB/rank "
-        f"nslices={w.nslices} plan={p}")
+    phase = {"ring": "allreduce", "staged": "allreduce_staged",
+             "reduce_scatter": "reduce_scatter_blocks", "all_gather": "all_gather_blocks"}[path]
+    p = rr.plan(w.R, blk if path in ("reduce_scatter", "all_gather") else w.count, w.dtype,
+                w.nslices, phase=phase, **opts)
+    log(f"workload {w.name} ({path}): R={w.R} {w.dtype} {w.op} "
+        f"{w.bytes_per_rank / 2**20:.1f} MiB/rank nslices={w.nslices} plan={p}")
 
     t = time.time()
     x = workloads.inputs(w)
     log(f"inputs generated in {time.time() - t:.1f} s")
-    torch_dt = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
-    raw_t = torch.int16 if w.dtype == "bf16" else torch.int32
-    raw_np = np.int16 if w.dtype == "bf16" else np.int32
+    torch_dt = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16,
+                "fp16": torch.float16}[w.dtype]
+    raw_t = torch.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else torch.int32
+    raw_np = np.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else np.int32
     slabs = rr.make_slabs(w.R, w.count, torch_dt, device="cuda")
     for r in range(w.R):
         slabs.ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
     pristine = slabs.storage.clone()
     stream = torch.cuda.current_stream()
+    kernel = "ring_kernel" if path == "ring" else "staged_kernel"
 
-    def step():
-        rr.allreduce_ring(slabs.ranks, w.op, w.nslices, **opts)
+    if path == "ring":
+        out_bufs = slabs.ranks
+
+        def step():
+            rr.allreduce_ring(slabs.ranks, w.op, w.nslices, **opts)
+    elif path == "staged":
+        out_bufs = rr.make_slabs(w.R, w.count, torch_dt, device="cuda").ranks
+
+        def step():
+            rr.allreduce_ring_staged(slabs.ranks, out_bufs, w.op, w.nslices, **opts)
+    elif path == "reduce_scatter":
+        out_bufs = [torch.empty(blk, dtype=torch_dt, device="cuda") for _ in range(w.R)]
+
+        def step():
+            rr.reduce_scatter(slabs.ranks, out_bufs, w.op, w.nslices, **opts)
+    else:
+        ag_send = [t[:blk] for t in slabs.ranks]
+        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
+
+        def step():
+            rr.all_gather(ag_send, out_bufs, w.nslices, **opts)
 
     # one checked call on the pristine inputs, kept for the CPU cross-check
     step()
     torch.cuda.synchronize()
     rr.check_kernel_error()
-    first_result = [slabs.ranks[r].view(raw_t).cpu().numpy() for r in range(w.R)]
+    first_result = [t.view(raw_t).cpu().numpy() for t in out_bufs]
 
     for _ in range(args.warmup):
         step()
@@ -181,10 +220,10 @@ def main():
     bytes_per_launch = B / per_call
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = stored_traffic(w.name, digest)
+    traffic = stored_traffic(w.name if path == "ring" else f"{path}_{w.name}", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "ring_kernel", "launch_ms_avg": round(avg_launch_ms, 5),
+                "kernel": kernel, "launch_ms_avg": round(avg_launch_ms, 5),
                 "launches_timed": args.steps * per_call, "bytes_per_launch": int(bytes_per_launch),
                 "kernel_source_digest": digest}
 
@@ -216,9 +255,17 @@ def main():
         runs, spent = 0, 0.0
         expect = None
         while runs == 0 or (spent < args.cpu_seconds and runs < 20):
-            bufs = [a.copy() for a in x]
             t = time.perf_counter()
-            oracle.allreduce(bufs, w.op)
+            if path == "ring":
+                bufs = [a.copy() for a in x]
+                t = time.perf_counter()
+                oracle.allreduce(bufs, w.op)
+            elif path == "staged":
+                bufs, _ = oracle.staged_allreduce(x, w.op)
+            elif path == "reduce_scatter":
+                bufs, _ = oracle.reduce_scatter_nccl(x, w.op)
+            else:
+                bufs, _ = oracle.all_gather_nccl([np.ascontiguousarray(a[:blk]) for a in x])
             spent += time.perf_counter() - t
             runs += 1
             expect = bufs
@@ -234,14 +281,15 @@ def main():
         log(f"cpu baseline: {cpu_baseline}")
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC if path == "ring" else f"{METRIC} ({path} path)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic", "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "config": {"workload": w.name, "R": w.R, "bytes_per_rank": w.bytes_per_rank,
+        "config": {"workload": w.name, "path": path, "R": w.R, "bytes_per_rank": w.bytes_per_rank,
                    "op": w.op, "nslices": w.nslices, "sync": p["sync"], "team": p["team"],
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
-                   "fused_boundary": bool(p["fused"]),
+                   "fused_boundary": bool(p["fused"]) if path == "ring" else False,
                    "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
     }

@@ -479,12 +479,14 @@ struct StagedArgs {
     uint32_t inject;
     int32_t R;
     int32_t team;
-    int32_t cols;          // lanes = workgroups per rank
+    int32_t cols;          // workgroups per rank
+    int32_t rounds;        // lane groups each workgroup runs one after another
     int32_t mode;
     int32_t k_first;       // steps this launch runs
     int32_t k_last;
     int32_t xcd_map;
     int32_t aligned;       // every operand 16-byte aligned: the vector path
+    int32_t pad;
 };
 
 // One step's data over n elements: in (the receive slot, device-scope loads),
@@ -577,8 +579,8 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
     constexpr int ES = ElemBytes<DT>::value;
     const int R = a.R;
     const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
-    const int r = pl.rank, lane = pl.col;
-    if (lane >= a.cols) return;  // padding column
+    const int r = pl.rank, col = pl.col;
+    if (col >= a.cols) return;  // padding column
     const int succ = r + 1 == R ? 0 : r + 1;
     const int pred = r == 0 ? R - 1 : r - 1;
     const bool synced = a.k_last > a.k_first;
@@ -594,6 +596,11 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
     __syncthreads();
     if (s_stop) return;
 
+    bool local = false, decided = false;
+    // Lane groups one after another (as in the in-place ring): only the lanes of
+    // one round are in flight, so a message is still cached when it is read.
+    for (int round = 0; round < a.rounds; ++round) {
+    const int lane = col + round * a.cols;
     const int j = lane / a.team, w = lane - j * a.team;
     const uint64_t off_lo = (uint64_t)j * a.slice_len + (uint64_t)w * a.sub_len;
     const uint64_t off_hi =
@@ -606,7 +613,6 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
         credit_base = a.credit_shadow[my_slot];
     }
     uint64_t credit_target = credit_base;
-    bool local = false, decided = false;
 
     for (int k = a.k_first; k <= a.k_last; ++k) {
         const bool has_in = k >= 1, has_send = k < K;
@@ -703,6 +709,7 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
         // every message this rank sends (K of them) is consumed and credited
         a.credit_shadow[my_slot] = credit_base + (uint64_t)K;
     }
+    }  // rounds
 }
 
 // ---------------------------------------------------------- barrier only --
@@ -1343,12 +1350,17 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     if (!kernel) return RR_ERR_INVALID;
     p->resident_max = resident_limit(d, kernel, kStagedBlock);
     const int target_cols = std::max(1, d->cus * 16 * 64 / kStagedBlock / R);
+    // rounds: one step of the lanes in flight (reads and writes of about three
+    // chunks per rank) within the Infinity Cache budget, as for the ring
+    const uint64_t step_bytes = 3ull * (uint64_t)R * p->chunk_len * es;
+    int rounds = opt && opt->rounds > 0 ? opt->rounds
+                                        : (int)std::max<uint64_t>(1, ceil_div(step_bytes, kRoundBytes));
     int team;
     if (opt && opt->team > 0) {
         team = opt->team;
     } else {
         const uint64_t by_size = std::max<uint64_t>(1, p->slice_len / V / ((uint64_t)kStagedBlock * 4));
-        const uint64_t wanted = ceil_div((uint64_t)target_cols, (uint64_t)nslices);
+        const uint64_t wanted = ceil_div((uint64_t)target_cols * rounds, (uint64_t)nslices);
         team = (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
     }
     const int max_team = std::max(1, kSlots / (R * nslices));
@@ -1356,10 +1368,15 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
         if (opt && opt->team > 0) return RR_ERR_UNSUPPORTED;
         team = max_team;
     }
+    const int lanes = nslices * team;
+    if (lanes % rounds != 0 || rounds > lanes) {  // rounds must divide the lanes
+        if (opt && opt->rounds > 0) return RR_ERR_UNSUPPORTED;
+        while (rounds > 1 && lanes % rounds != 0) --rounds;
+    }
     p->team = team;
     p->depth = 1;
-    p->rounds = 1;
-    p->cols = nslices * team;
+    p->rounds = rounds;
+    p->cols = lanes / rounds;
     p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
     p->xcd_map = (flags & RR_FLAG_NO_XCD_MAP) ? 0 : 1;
     const uint64_t cols_launched = p->xcd_map ? round_up((uint64_t)p->cols, 8) : p->cols;
@@ -1385,6 +1402,7 @@ static rr_status_t check_staged_args(const void* const* send, void* const* recv,
     if (opt) {
         if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
         if (opt->team < 0 || opt->team > 4096) return RR_ERR_INVALID;
+        if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
         if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
             return RR_ERR_INVALID;
     }
@@ -1486,6 +1504,7 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
     a.R = R;
     a.team = p.team;
     a.cols = p.cols;
+    a.rounds = p.rounds;
     a.mode = mode;
     a.xcd_map = p.xcd_map;
     a.aligned = mode == MODE_ALLREDUCE || (n * es) % 16 == 0;

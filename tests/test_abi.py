@@ -102,6 +102,7 @@ B = A + (1 << 30)  # a second region, far from the first
     dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, op=9),
     dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, nslices=0),
     dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, sync=9),
+    dict(send=[A, A + 4096], recv=[B, B + 4096], n=16, rounds=-1),
     dict(send=[A, A + 4096], recv=[B, B + 4096], n=(1 << 40) + 1),
 ])
 def test_staged_invalid_arguments(rr, kind, case):

@@ -101,6 +101,24 @@ def test_staged_repeat_and_team(rr):
         assert_matches_oracle(got, want, "fp16", f"staged {opts}")
 
 
+@pytest.mark.parametrize("rounds,team", [(2, 4), (4, 4), (3, 3), (8, 2)])
+def test_staged_rounds(rr, rounds, team):
+    """Lane groups run one after another: the same bits for every grouping."""
+    R, count, ns = 8, (1 << 20) + 13, 4
+    p = rr.plan(R, count, "bf16", ns, phase="allreduce_staged", rounds=rounds, team=team)
+    assert p["rounds"] == rounds and p["team"] == team
+    log(f"case staged rounds={rounds} team={team} plan={p}")
+    x = workloads.generate(R, count, "bf16", "normal", 65)
+    got = _staged(rr, x, "bf16", "sum", ns, rounds=rounds, team=team)
+    assert_matches_oracle(got, oracle_expect(x, "sum"), "bf16", f"staged rounds {rounds}")
+    y = workloads.generate(R, R * 5001, "fp32", "uniform_pm1", 66)
+    recv = rr.reduce_scatter(_blocks_send(y, "fp32"), None, "sum", ns, rounds=rounds, team=team)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    want, _ = oracle.reduce_scatter_nccl(y, "sum")
+    assert_matches_oracle([to_host(t, "fp32") for t in recv], want, "fp32", "RS rounds")
+
+
 def test_staged_single_rank_and_empty(rr):
     x = torch.randn(1000, device="cuda")
     y = rr.allreduce_ring_staged([x])[0]
