@@ -53,10 +53,11 @@ def parse():
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--path", default="ring",
-                    choices=["ring", "staged", "reduce_scatter", "all_gather"],
+                    choices=["ring", "staged", "reduce_scatter", "all_gather", "alltoall"],
                     help="ring: the in-place ring (headline); staged: the out-of-place staged "
                          "primitives; reduce_scatter / all_gather: the standalone collectives "
-                         "over the same per-rank buffer (R blocks / one block per rank)")
+                         "over the same per-rank buffer (R blocks / one block per rank); "
+                         "alltoall: the per-rank buffer as R blocks, one per receiver")
     ap.add_argument("--fused", action="store_true",
                     help="fuse the last ReduceScatter hop with the first AllGather hop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,9 +143,11 @@ def main():
     blk = w.count // w.R
     rr.init()
     phase = {"ring": "allreduce", "staged": "allreduce_staged",
-             "reduce_scatter": "reduce_scatter_blocks", "all_gather": "all_gather_blocks"}[path]
-    p = rr.plan(w.R, blk if path in ("reduce_scatter", "all_gather") else w.count, w.dtype,
-                w.nslices, phase=phase, **opts)
+             "reduce_scatter": "reduce_scatter_blocks", "all_gather": "all_gather_blocks",
+             "alltoall": "alltoall"}[path]
+    p = rr.plan(w.R, blk if path in ("reduce_scatter", "all_gather", "alltoall") else w.count,
+                w.dtype, w.nslices, phase=phase,
+                **({} if path == "alltoall" else opts))
     log(f"workload {w.name} ({path}): R={w.R} {w.dtype} {w.op} "
         f"{w.bytes_per_rank / 2**20:.1f} MiB/rank nslices={w.nslices} plan={p}")
 
@@ -160,7 +163,7 @@ def main():
         slabs.ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
     pristine = slabs.storage.clone()
     stream = torch.cuda.current_stream()
-    kernel = "ring_kernel" if path == "ring" else "staged_kernel"
+    kernel = {"ring": "ring_kernel", "alltoall": "alltoall_kernel"}.get(path, "staged_kernel")
 
     if path == "ring":
         out_bufs = slabs.ranks
@@ -177,12 +180,17 @@ def main():
 
         def step():
             rr.reduce_scatter(slabs.ranks, out_bufs, w.op, w.nslices, **opts)
-    else:
+    elif path == "all_gather":
         ag_send = [t[:blk] for t in slabs.ranks]
         out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
 
         def step():
             rr.all_gather(ag_send, out_bufs, w.nslices, **opts)
+    else:
+        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
+
+        def step():
+            rr.alltoall(slabs.ranks, out_bufs)
 
     # one checked call on the pristine inputs, kept for the CPU cross-check
     step()
@@ -264,6 +272,8 @@ def main():
                 bufs, _ = oracle.staged_allreduce(x, w.op)
             elif path == "reduce_scatter":
                 bufs, _ = oracle.reduce_scatter_nccl(x, w.op)
+            elif path == "alltoall":
+                bufs = oracle.alltoall(x)
             else:
                 bufs, _ = oracle.all_gather_nccl([np.ascontiguousarray(a[:blk]) for a in x])
             spent += time.perf_counter() - t

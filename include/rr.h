@@ -274,10 +274,27 @@ rr_status_t all_gather(const void *const *sendbufs, void *const *recvbufs, int R
                        size_t sendcount, rr_dtype_t dt, int nslices, const rr_options_t *opt,
                        rr_stream_t stream);
 
+/* ---------------------------------------------------------------- AlltoAll */
+
+/* The pure AlltoAll of the 2kiu.com article on NCCL GIN (section "a pure GIN
+   AlltoAll kernel"): sendbufs[r] and recvbufs[r] hold R blocks of `count`
+   elements; afterwards block r of recvbufs[q] is block q of sendbufs[r], bit
+   for bit.  Each workgroup puts its part of rank r's R blocks and then adds 1
+   to every receiver's counting signal; one workgroup per receiver waits for
+   all R * parts arrivals (R when a block is one part), advancing a persisted
+   shadow, so the signal never needs a reset or an entry barrier.  Buffers
+   16-byte aligned and pairwise disjoint; any count.  Traffic 2 * R * R * count
+   * elem bytes.  Options: timeout_ns, inject, flags (sync AUTO or P2P).
+   Errors: RR_ERR_INVALID (bad sizes, NULL, misaligned or overlapping
+   buffers), RR_ERR_UNSUPPORTED (grid not resident), RR_ERR_HIP. */
+rr_status_t alltoall(const void *const *sendbufs, void *const *recvbufs, int R, size_t count,
+                     rr_dtype_t dt, const rr_options_t *opt, rr_stream_t stream);
+
 /* The plan a call with these arguments would run; no device work.  `phase` is
    0 for AllReduce, 1 for ReduceScatter, 2 for AllGather (the in-place ring),
    3 for allreduce_ring_staged, 4 for reduce_scatter (count = recvcount), 5 for
-   all_gather (count = sendcount).  Errors as the call. */
+   all_gather (count = sendcount), 6 for alltoall (count per block; team =
+   parts per block).  Errors as the call. */
 rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int phase,
                           const rr_options_t *opt, rr_plan_t *out);
 

@@ -83,6 +83,8 @@ def _bind(lib):
     lib.ro_reduce_scatter_nccl.argtypes = lib.ro_staged_allreduce.argtypes
     lib.ro_all_gather_nccl.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, u64, i32,
                                        ctypes.POINTER(_StepLog)]
+    lib.ro_alltoall.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, u64, i32]
+    lib.ro_alltoall.restype = ctypes.c_int
     for f in (lib.ro_chunk_bounds, lib.ro_allreduce, lib.ro_reduce_scatter, lib.ro_all_gather,
               lib.ro_allreduce_at, lib.ro_direct_sum_f64, lib.ro_staged_allreduce,
               lib.ro_reduce_scatter_nccl, lib.ro_all_gather_nccl):
@@ -322,3 +324,19 @@ def all_gather_nccl(send, log: bool = False):
     recv = [np.zeros(R * n, dtype=NP_DTYPES[dt]) for _ in range(R)]
     steps = _staged(_load().ro_all_gather_nccl, send, recv, n, (DTYPES[dt],), log)
     return recv, steps
+
+
+def alltoall(send):
+    """send[r] holds R blocks; returns recv with recv[q] block r = send[r] block q."""
+    R = len(send)
+    total = send[0].size
+    if total % R:
+        raise ValueError("send buffers must hold R equal blocks")
+    for b in send:
+        if not b.flags.c_contiguous or b.dtype != send[0].dtype or b.size != total:
+            raise ValueError("send buffers must be contiguous, same dtype, same length")
+    recv = [np.empty_like(send[0]) for _ in range(R)]
+    sp = (ctypes.c_void_p * R)(*[b.ctypes.data for b in send])
+    rp = (ctypes.c_void_p * R)(*[b.ctypes.data for b in recv])
+    _check(_load().ro_alltoall(sp, rp, R, total // R, send[0].itemsize), "alltoall")
+    return recv

@@ -615,4 +615,21 @@ int ro_all_gather_nccl(const void *const *send, void *const *recv, int R, uint64
     return staged(send, recv, R, sendcount, dt, RO_SUM, STAGED_AG, log);
 }
 
+/* ------------------------------------------------------------- AlltoAll */
+
+/* The pure AlltoAll of the 2kiu.com article on NCCL GIN (section "a pure GIN
+ * AlltoAll kernel"): every rank puts block q of its send buffer into rank q's
+ * receive buffer at block position (its own rank), so recv[q] block r =
+ * send[r] block q.  A byte copy; blocks of `count` elements of `es` bytes. */
+int ro_alltoall(const void *const *send, void *const *recv, int R, uint64_t count, int es)
+{
+    if (R < 1 || R > RO_MAX_RANKS || (es != 2 && es != 4) || !send || !recv) return RO_EINVAL;
+    uint64_t bytes = count * (uint64_t)es;
+    for (int r = 0; r < R; ++r)
+        for (int q = 0; q < R; ++q)
+            memcpy((char *)recv[q] + (uint64_t)r * bytes, (const char *)send[r] + (uint64_t)q * bytes,
+                   bytes);
+    return RO_OK;
+}
+
 int ro_abi_version(void) { return 1; }

@@ -35,7 +35,7 @@ OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
 SYNCS = {"auto": 0, "p2p": 1, "barrier": 2, "launch": 3, "per_peer": 4}
 SYNC_NAMES = {v: k for k, v in SYNCS.items()}
 PHASES = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "allreduce_staged": 3,
-          "reduce_scatter_blocks": 4, "all_gather_blocks": 5}
+          "reduce_scatter_blocks": 4, "all_gather_blocks": 5, "alltoall": 6}
 
 STATUS = {0: "RR_OK", 1: "RR_ERR_INVALID", 2: "RR_ERR_UNSUPPORTED", 3: "RR_ERR_HIP",
           4: "RR_ERR_TIMEOUT", 5: "RR_ERR_NOMEM"}
@@ -111,6 +111,7 @@ _reduce_scatter = _sig("reduce_scatter", _i, ctypes.POINTER(_vp), ctypes.POINTER
                        _i, _i, _OPT, _vp)
 _all_gather = _sig("all_gather", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i, _i,
                    _OPT, _vp)
+_alltoall = _sig("alltoall", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i, _OPT, _vp)
 _cb_create = _sig("counting_barrier_create", _i, _i, _i, ctypes.POINTER(_vp))
 _cb_destroy = _sig("counting_barrier_destroy", _i, _vp)
 _cb_reset = _sig("counting_barrier_reset", _i, _vp, _vp)
@@ -131,7 +132,7 @@ _finalize = _sig("rr_finalize", None)
 # Every symbol include/rr.h declares, for the export check.
 EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
             "reduce_scatter_ring_ex", "all_gather_ring_ex", "allreduce_ring_staged",
-            "reduce_scatter", "all_gather", "rr_plan_query",
+            "reduce_scatter", "all_gather", "alltoall", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
             "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
             "counting_barrier_early_passes", "counting_barrier_run",
@@ -308,6 +309,23 @@ def all_gather(send, recv=None, nslices: int = 1, *, stream=None, **opts):
     return recv
 
 
+def alltoall(send, recv=None, *, stream=None, **opts):
+    """AlltoAll: send[r] and recv[r] hold R blocks; recv[q] block r = send[r]
+    block q.  Returns recv."""
+    R = len(send)
+    total = send[0].numel()
+    if total % R:
+        raise ValueError("buffers must hold R equal blocks")
+    if recv is None:
+        recv = [torch.empty_like(t) for t in send]
+    sp, rp, dt = _pair(send, recv, total, total)
+    with torch.cuda.device(send[0].device):
+        o = _options(**opts)
+        st = _alltoall(sp, rp, R, total // R, DTYPES[dt], ctypes.byref(o), _stream_handle(stream))
+    _check(st, "alltoall")
+    return recv
+
+
 def staged_ptrs(kind: str, send, recv, n: int, dtype, op="sum", nslices: int = 1, stream=0,
                 **opts) -> int:
     """Raw-pointer call of the staged entry points; returns the status."""
@@ -321,6 +339,8 @@ def staged_ptrs(kind: str, send, recv, n: int, dtype, op="sum", nslices: int = 1
         return _allreduce_ring_staged(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
     if kind == "reduce_scatter":
         return _reduce_scatter(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
+    if kind == "alltoall":
+        return _alltoall(sp, rp, R, n, dt, ctypes.byref(o), stream)
     return _all_gather(sp, rp, R, n, dt, nslices, ctypes.byref(o), stream)
 
 

@@ -448,6 +448,8 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
 //                   (r - k) mod R.
 constexpr int kFifoSlots = 2;
 constexpr int kStagedBlock = 512;
+constexpr int kA2ABlock = 256;
+constexpr int kA2AWavesPerCU = 4;
 enum : int { MODE_ALLREDUCE = 0, MODE_RS = 1, MODE_AG = 2 };
 enum : int { P_SEND = 0, P_RRS = 1, P_RRCS = 2, P_RCS = 3, P_RECV = 4, P_RRC = 5, P_CS = 6 };
 
@@ -710,6 +712,91 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
         a.credit_shadow[my_slot] = credit_base + (uint64_t)K;
     }
     }  // rounds
+}
+
+// ---------------------------------------------------------------- AlltoAll
+//
+// The pure AlltoAll of the 2kiu.com article on NCCL GIN (section "a pure GIN
+// AlltoAll kernel"): every rank puts block q of its send buffer into rank q's
+// receive buffer at block position (its own rank), each put followed by one
+// increment of the receiver's counting signal, and one receiving workgroup per
+// rank waits until all the arrivals it expects have landed.  Workgroup (rank r,
+// part p) copies part p of its R blocks, releases its stores at agent scope,
+// then adds 1 to each receiver's signal; so a receiver expects R * parts
+// arrivals per call (R with one part).  The waiter advances a persisted shadow
+// (the article's per-signal shadows) instead of reading the signal at entry,
+// which is why no entry barrier is needed here: there is no base value to race
+// with.
+struct A2AArgs {
+    const void* send[kMaxDevices];
+    void* recv[kMaxDevices];
+    uint64_t count;     // elements per block
+    uint64_t part_len;  // elements per part (a vector multiple)
+    uint64_t* sig;      // one counting signal per receiver
+    uint64_t* shadow;
+    ErrorRecord* err;
+    uint64_t timeout_ticks;
+    int32_t R;
+    int32_t parts;
+    int32_t aligned;
+    uint32_t inject;
+};
+
+template <int ES, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) alltoall_kernel(const A2AArgs a) {
+    constexpr int V = 16 / ES;
+    constexpr int U = 8;
+    const int R = a.R;
+    const int r = (int)blockIdx.x / a.parts;
+    const int part = (int)blockIdx.x - r * a.parts;
+    __shared__ int s_stop;
+    if (threadIdx.x == 0) s_stop = sig_read(&a.err->flag) != 0;  // sticky failure
+    __syncthreads();
+    if (s_stop) return;
+    const uint64_t lo = (uint64_t)part * a.part_len;
+    const uint64_t hi = umin(lo + a.part_len, a.count);
+    for (int i = 0; i < R && lo < hi; ++i) {
+        const int q = (r + 1 + i) % R;  // start at the successor: spread the receivers
+        const char* src = (const char*)a.send[r] + ((uint64_t)q * a.count + lo) * ES;
+        char* dst = (char*)a.recv[q] + ((uint64_t)r * a.count + lo) * ES;
+        const uint64_t n = hi - lo;
+        uint64_t done = 0;
+        if (a.aligned) {
+            const u32x4* __restrict__ s4 = (const u32x4*)src;
+            u32x4* __restrict__ d4 = (u32x4*)dst;
+            const uint64_t nv = n / V;
+            uint64_t v = threadIdx.x;
+            for (; v + (U - 1) * BLOCK < nv; v += U * BLOCK) {
+                u32x4 x[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(&s4[v + u * BLOCK]);
+#pragma unroll
+                for (int u = 0; u < U; ++u) d4[v + u * BLOCK] = x[u];
+            }
+            for (; v < nv; v += BLOCK) d4[v] = __builtin_nontemporal_load(&s4[v]);
+            done = nv * V;
+        }
+        for (uint64_t t = done + threadIdx.x; t < n; t += BLOCK) {
+            if constexpr (ES == 2)
+                ((uint16_t*)dst)[t] = ((const uint16_t*)src)[t];
+            else
+                ((uint32_t*)dst)[t] = ((const uint32_t*)src)[t];
+        }
+    }
+    // the puts have landed before the receivers are told (agent scope: the
+    // receiver may run on another XCD)
+    release_stores(false);
+    __syncthreads();
+    const bool drop = (a.inject & RR_INJECT_DROP_ARRIVAL) && r == 0 && part == 0;
+    if (!drop && (int)threadIdx.x < R) sig_add(&a.sig[(uint64_t)threadIdx.x * kSignalStride], 1);
+    if (part == 0 && threadIdx.x == 0) {  // the receiving workgroup of rank r
+        uint64_t target = a.shadow[r] + (uint64_t)R * a.parts;
+        if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && r == 0) target += 1;
+        const WaitResult res = sig_wait(&a.sig[(uint64_t)r * kSignalStride], target, a.err,
+                                        a.timeout_ticks);
+        if (res.status == WAIT_TIMEOUT) record_timeout(a.err, 0, r, 0, target, res.observed);
+        if (res.status == WAIT_OK) a.shadow[r] = target;
+    }
 }
 
 // ---------------------------------------------------------- barrier only --
@@ -1522,6 +1609,96 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
     return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
 }
 
+// ------------------------------------------------------------- AlltoAll, host
+
+static rr_status_t make_a2a_plan(const DeviceState* d, int R, uint64_t count, int dt,
+                                 const rr_options_t* opt, Plan* p) {
+    const uint64_t es = elem_bytes(dt);
+    const uint64_t V = 16 / es;
+    const void* kernel = es == 2 ? (const void*)alltoall_kernel<2, kA2ABlock>
+                                 : (const void*)alltoall_kernel<4, kA2ABlock>;
+    p->block = kA2ABlock;
+    p->resident_max = resident_limit(d, kernel, kA2ABlock);
+    // parts per block: about kA2AWavesPerCU waves per CU in all, every
+    // workgroup resident (the receiving workgroups wait for the others)
+    const uint64_t by_size = std::max<uint64_t>(1, count / V / ((uint64_t)kA2ABlock * 8));
+    const uint64_t wanted = std::max<uint64_t>(
+        1, std::min<uint64_t>((uint64_t)d->cus * kA2AWavesPerCU * 64 / kA2ABlock,
+                              (uint64_t)p->resident_max) / (uint64_t)R);
+    int parts = opt && opt->team > 0 ? opt->team
+                                     : (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
+    p->team = parts;
+    p->cols = parts;
+    p->rounds = 1;
+    p->depth = 1;
+    p->fuse = 0;
+    p->chunk_len = count;
+    p->slice_len = count;
+    p->sub_len = round_up(ceil_div(count, (uint64_t)parts), V);
+    p->grid = R * parts;
+    p->sync = RR_SYNC_P2P;
+    p->launches = 1;
+    p->xcd_map = 0;
+    p->coop = 0;
+    p->g_first = p->g_last = 0;
+    p->hbm_bytes = 2ull * R * R * count * es;
+    if (p->grid > p->resident_max) return RR_ERR_UNSUPPORTED;
+    return RR_OK;
+}
+
+static rr_status_t run_alltoall(const void* const* send, void* const* recv, int R, uint64_t count,
+                                int dt, const rr_options_t* opt, rr_stream_t stream) {
+    if (R < 1 || R > RR_MAX_RANKS || !valid_dtype(dt)) return RR_ERR_INVALID;
+    if ((uint64_t)R * count > (uint64_t)1 << 40) return RR_ERR_INVALID;
+    if (opt && (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_P2P)) return RR_ERR_INVALID;
+    if (opt && (opt->team < 0 || opt->team > 65536)) return RR_ERR_INVALID;
+    if (!send || !recv) return RR_ERR_INVALID;
+    if (count == 0) return RR_OK;
+    const uint64_t es = elem_bytes(dt);
+    const uint64_t bytes = (uint64_t)R * count * es;
+    std::vector<std::pair<uintptr_t, uint64_t>> iv;
+    for (int r = 0; r < R; ++r) {
+        if (!send[r] || !recv[r]) return RR_ERR_INVALID;
+        if ((uintptr_t)send[r] % 16 || (uintptr_t)recv[r] % 16) return RR_ERR_INVALID;
+        iv.push_back({(uintptr_t)send[r], bytes});
+        iv.push_back({(uintptr_t)recv[r], bytes});
+    }
+    std::sort(iv.begin(), iv.end());
+    for (size_t i = 0; i + 1 < iv.size(); ++i)
+        if (iv[i].first + iv[i].second > iv[i + 1].first) return RR_ERR_INVALID;
+    DeviceState* d = nullptr;
+    rr_status_t st = ensure_device(&d);
+    if (st != RR_OK) return st;
+    if (!(opt && (opt->flags & RR_FLAG_NO_POINTER_CHECK))) {
+        if ((st = check_extents((void* const*)send, R, bytes)) != RR_OK) return st;
+        if ((st = check_extents(recv, R, bytes)) != RR_OK) return st;
+    }
+    Plan p;
+    if ((st = make_a2a_plan(d, R, count, dt, opt, &p)) != RR_OK) return st;
+    A2AArgs a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < R; ++r) {
+        a.send[r] = send[r];
+        a.recv[r] = recv[r];
+    }
+    a.count = count;
+    a.part_len = p.sub_len;
+    a.sig = d->sig;        // receiver q uses slot q (lane 0 of the ring layout)
+    a.shadow = d->shadow;
+    a.err = d->err;
+    a.timeout_ticks = timeout_ticks(d, opt);
+    a.R = R;
+    a.parts = p.cols;
+    a.aligned = (count * es) % 16 == 0;
+    a.inject = opt ? opt->inject : 0;
+    hipStream_t s = (hipStream_t)stream;
+    if (es == 2)
+        hipLaunchKernelGGL((alltoall_kernel<2, kA2ABlock>), dim3(p.grid), dim3(kA2ABlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((alltoall_kernel<4, kA2ABlock>), dim3(p.grid), dim3(kA2ABlock), 0, s, a);
+    return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
+}
+
 static rr_status_t fill(uint64_t* p, uint64_t n, uint64_t value, uint64_t stride, hipStream_t s) {
     if (n == 0) return RR_OK;
     const unsigned grid = (unsigned)std::min<uint64_t>(1024, ceil_div(n, 256));
@@ -1597,9 +1774,14 @@ rr_status_t all_gather(const void* const* sendbufs, void* const* recvbufs, int R
     return run_staged(sendbufs, recvbufs, R, sendcount, dt, RR_SUM, nslices, MODE_AG, opt, stream);
 }
 
+rr_status_t alltoall(const void* const* sendbufs, void* const* recvbufs, int R, size_t count,
+                     rr_dtype_t dt, const rr_options_t* opt, rr_stream_t stream) {
+    return run_alltoall(sendbufs, recvbufs, R, count, dt, opt, stream);
+}
+
 rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int phase,
                           const rr_options_t* opt, rr_plan_t* out) {
-    if (!out || phase < 0 || phase > 5) return RR_ERR_INVALID;
+    if (!out || phase < 0 || phase > 6) return RR_ERR_INVALID;
     if (R < 1 || R > RR_MAX_RANKS || nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
     if (!valid_dtype(dt)) return RR_ERR_INVALID;
     DeviceState* d = nullptr;
@@ -1608,8 +1790,10 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
     Plan p;
     if (phase <= 2)
         st = make_plan(d, R, count, dt, RR_SUM, nslices, phase, opt, &p);
-    else
+    else if (phase <= 5)
         st = make_staged_plan(d, R, count, dt, RR_SUM, nslices, phase - 3, opt, &p);
+    else
+        st = make_a2a_plan(d, R, count, dt, opt, &p);
     if (st != RR_OK) return st;
     out->sync = p.sync;
     out->team = p.team;

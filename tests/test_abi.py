@@ -88,7 +88,7 @@ def test_invalid_arguments_rejected_on_host(rr, case):
 B = A + (1 << 30)  # a second region, far from the first
 
 
-@pytest.mark.parametrize("kind", ["allreduce", "reduce_scatter", "all_gather"])
+@pytest.mark.parametrize("kind", ["allreduce", "reduce_scatter", "all_gather", "alltoall"])
 @pytest.mark.parametrize("case", [
     dict(send=[], recv=[], n=16),                                              # R = 0
     dict(send=[A + i * 4096 for i in range(65)], recv=[B + i * 4096 for i in range(65)], n=16),
@@ -106,8 +106,10 @@ B = A + (1 << 30)  # a second region, far from the first
     dict(send=[A, A + 4096], recv=[B, B + 4096], n=(1 << 40) + 1),
 ])
 def test_staged_invalid_arguments(rr, kind, case):
-    if kind == "all_gather" and "op" in case:
-        pytest.skip("all_gather takes no op")
+    if kind in ("all_gather", "alltoall") and "op" in case:
+        pytest.skip(f"{kind} takes no op")
+    if kind == "alltoall" and ("nslices" in case or "rounds" in case):
+        pytest.skip("alltoall takes no slices or rounds")
     kw = dict(case)
     st = rr.staged_ptrs(kind, kw.pop("send"), kw.pop("recv"), kw.pop("n"), kw.pop("dtype", "fp32"),
                         kw.pop("op", "sum"), kw.pop("nslices", 1), **kw)
@@ -166,7 +168,7 @@ def test_copy_rejects_bad_arguments(rr):
 def test_plan_query_rejects_bad_arguments(rr):
     p = rr._Plan()
     assert rr._plan_query(0, 16, 1, 1, 0, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
-    assert rr._plan_query(4, 16, 1, 1, 6, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
+    assert rr._plan_query(4, 16, 1, 1, 7, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
     assert rr._plan_query(4, 16, 4, 1, 0, None, ctypes.byref(p)) == rr.RR_ERR_INVALID
     assert rr._plan_query(4, 16, 1, 1, 0, None, None) == rr.RR_ERR_INVALID
 

@@ -183,3 +183,29 @@ def test_single_rank_is_a_copy():
         assert np.array_equal(_bits(y[0], dtype), _bits(x[0], dtype))
         y, _ = oracle.all_gather_nccl(x)
         assert np.array_equal(_bits(y[0], dtype), _bits(x[0], dtype))
+
+
+# ---------------------------------------------------------------- AlltoAll
+
+@pytest.mark.parametrize("R,n", [(1, 5), (2, 3), (4, 16), (8, 37), (16, 9)])
+def test_alltoall_pattern_of_the_gin_sample(R, n):
+    """The GIN article's AlltoAll sample fills rank r's block for rank d with
+    r*1000 + d*100 + i and checks that rank d receives, at block r, exactly
+    that: the same pattern here (int32), so each block's source and place are
+    both visible."""
+    i = np.arange(n, dtype=np.int64)
+    send = [np.concatenate([r * 1000 + d * 100 + i for d in range(R)]).astype(np.int32)
+            for r in range(R)]
+    recv = oracle.alltoall(send)
+    for d in range(R):
+        for r in range(R):
+            assert np.array_equal(recv[d][r * n:(r + 1) * n], (r * 1000 + d * 100 + i).astype(np.int32))
+
+
+def test_alltoall_is_a_byte_copy():
+    R, n = 5, 33
+    x = workloads.generate(R, R * n, "fp16", "bits", 3)   # NaN payloads included
+    y = oracle.alltoall(x)
+    z = oracle.alltoall(y)                                  # the exchange is its own inverse
+    for a, b in zip(x, z):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
