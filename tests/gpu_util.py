@@ -46,14 +46,18 @@ def to_host(t, dtype):
 def guards_intact(slabs, dtype, count):
     """Everything outside the R rank buffers still holds the fill pattern."""
     st = slabs.storage
-    mask = torch.ones(st.numel(), dtype=torch.bool, device=st.device)
-    for r in range(len(slabs.ranks)):
-        mask[r * slabs.stride: r * slabs.stride + count] = False
-    outside = st[mask]
-    if outside.numel() == 0:
-        return True
-    ref = torch.full_like(outside, GUARD_FILL[dtype])
-    return bool(torch.equal(outside.view(RAW_TORCH[dtype]), ref.view(RAW_TORCH[dtype])))
+    R = len(slabs.ranks)
+    # the gap after each rank buffer (the last one runs to the end of the storage)
+    gaps = [(r * slabs.stride + count, (r + 1) * slabs.stride if r + 1 < R else st.numel())
+            for r in range(R)]
+    for lo, hi in gaps:
+        if hi <= lo:
+            continue
+        piece = st[lo:hi]
+        ref = torch.full_like(piece, GUARD_FILL[dtype])
+        if not torch.equal(piece.view(RAW_TORCH[dtype]), ref.view(RAW_TORCH[dtype])):
+            return False
+    return True
 
 
 def bits_equal(a, b, dtype):

@@ -388,3 +388,8 @@ def test_full_fused_boundary(rr, w):
 def test_full_r16_sweep(rr, k):
     for op, ns in (("sum", 16), ("max", 1 + (k % 4) * 5)):
         _full_size(rr, workloads.r16_sweep(k, op, ns), 4000)
+
+
+def test_full_r16_1GiB(rr):
+    """The largest point of the R=16 sweep: 1 GiB per rank, 16 GiB in all."""
+    _full_size(rr, workloads.r16_sweep(9, "sum", 16), 3000)
