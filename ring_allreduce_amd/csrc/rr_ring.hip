@@ -48,6 +48,7 @@ constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
 // Bytes one hop of the lanes in flight may move before a partial written in
 // that hop risks leaving the 256 MB Infinity Cache before it is read back.
 constexpr uint64_t kRoundBytes = 192ull << 20;
+constexpr uint64_t kLongNapBytes = 64ull << 20;
 // Lanes a workgroup interleaves when the caller does not choose: a per-hop
 // barrier waits for the slowest of R workgroups, which a second lane hides; a
 // predecessor hand-off is cheap enough that a second lane costs more than it
@@ -78,6 +79,7 @@ struct RingArgs {
     int32_t cols;        // workgroups per rank = grid / R
     int32_t rounds;      // lane groups each workgroup runs one after another
     int32_t depth;       // lanes each workgroup interleaves hop by hop (1..kMaxDepth)
+    int32_t long_nap;    // barrier waits poll slowly (a hop moves enough data to hide it)
 };
 
 __device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -353,7 +355,8 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
                             g == a.g_first + 1)
                             target += 1;
                         const WaitResult res = sig_wait(&a.sig[(uint64_t)my_slot * kSignalStride],
-                                                        target, a.err, a.timeout_ticks);
+                                                        target, a.err, a.timeout_ticks,
+                                                        a.long_nap != 0);
                         if (res.status == WAIT_TIMEOUT)
                             record_timeout(a.err, lane[p], r, g, target, res.observed);
                         shadow[p] = target;
@@ -1041,6 +1044,7 @@ std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
 struct Plan {
+    int long_nap;
     int fuse;
     int sync;
     int team;
@@ -1345,6 +1349,10 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     p->sync = sync;
     p->launches = sync == RR_SYNC_LAUNCH ? p->g_last - p->g_first + 1 : 1;
     p->coop = sync != RR_SYNC_LAUNCH && (flags & RR_FLAG_COOPERATIVE) ? 1 : 0;
+    // barrier waits poll slowly once one hop moves at least kLongNapBytes over
+    // all ranks (about 10 us of traffic, so a later wake-up of up to ~2 us is
+    // hidden; smaller buffers are latency-bound and keep the fast poll)
+    p->long_nap = sync == RR_SYNC_BARRIER && 3ull * count * elem_bytes(dt) >= kLongNapBytes;
     return RR_OK;
 }
 
@@ -1382,6 +1390,7 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.rounds = p.rounds;
     a.depth = p.depth;
     a.fuse = p.fuse;
+    a.long_nap = p.long_nap;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
     RingKernel k = pick_ring_kernel(dt, op, p.block);
