@@ -221,6 +221,21 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}) "
         f"-> {value:.1f} GB/s algorithmic")
 
+    # Per-call spread: each of K further calls between its own pair of events
+    # (outside the timed region above, so `value` is unaffected).
+    per_call_ms = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    per_call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    timing = {"calls": len(per_call_ms), "median_ms": round(per_call_ms[len(per_call_ms) // 2], 5),
+              "min_ms": round(per_call_ms[0], 5), "max_ms": round(per_call_ms[-1], 5)}
+
     # The ring kernel's average launch duration: HIP events on the launch stream
     # around the timed region, divided by the launches it holds (back to back).
     per_call = p["launches"]
@@ -254,7 +269,23 @@ def main():
         ms = a.elapsed_time(b) / reps
         copy_ceiling = {"bytes": 2 * n, "ms": round(ms, 4),
                         "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-        del src, dst
+        # a 2-read + 1-write stream (the shape of a ReduceScatter hop): torch's
+        # elementwise add over 1 GiB fp32 operands, as a reference only
+        fa = src.view(torch.float32)
+        fb = dst.view(torch.float32)
+        fc = torch.empty_like(fa)
+        for _ in range(3):
+            torch.add(fa, fb, out=fc)
+        a.record(stream)
+        for _ in range(reps):
+            torch.add(fa, fb, out=fc)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms2 = a.elapsed_time(b) / reps
+        copy_ceiling["read2_write1"] = {"bytes": 3 * n, "ms": round(ms2, 4),
+                                        "GB/s": round(3 * n / (ms2 * 1e-3) / 1e9, 1),
+                                        "kernel": "torch.add (reference)"}
+        del src, dst, fc
         log(f"copy ceiling: {copy_ceiling}")
 
     cpu_baseline = None
@@ -262,7 +293,7 @@ def main():
         import oracle  # test infrastructure: the CPU baseline leg only
         runs, spent = 0, 0.0
         expect = None
-        while runs == 0 or (spent < args.cpu_seconds and runs < 20):
+        while runs == 0 or (spent < args.cpu_seconds and runs < 1000):
             t = time.perf_counter()
             if path == "ring":
                 bufs = [a.copy() for a in x]
@@ -301,6 +332,10 @@ def main():
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
                    "fused_boundary": bool(p["fused"]) if path == "ring" else False,
                    "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
+        "timing": timing,
+        # ring traffic in the sources' sense: bytes sent over all links per call
+        "bus_bytes_per_step": (2 * (w.R - 1) * w.bytes_per_rank if path in ("ring", "staged")
+                               else (w.R - 1) * w.bytes_per_rank),
         "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
     }
     print(json.dumps(out), flush=True)
