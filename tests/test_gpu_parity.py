@@ -393,3 +393,31 @@ def test_full_r16_sweep(rr, k):
 def test_full_r16_1GiB(rr):
     """The largest point of the R=16 sweep: 1 GiB per rank, 16 GiB in all."""
     _full_size(rr, workloads.r16_sweep(9, "sum", 16), 3000)
+
+
+def test_pieces_longer_than_one_descriptor(rr):
+    """A workgroup's range over 1 GiB is moved in parts (each buffer descriptor
+    covers at most 1 GiB): R=2, 2 GiB per rank, one slice, one team member, in
+    the ring and in the staged loop."""
+    R, count = 2, (1 << 29) + 37          # fp32: 2 GiB + 148 B per rank
+    w = workloads.Workload("r2_fp32_2GiB", R, "fp32", "sum", count, 1, 97, "uniform_pm1")
+    p = rr.plan(R, count, "fp32", 1, team=1)
+    assert p["sub_len"] * 4 > (1 << 30)
+    log(f"case big pieces plan={p}")
+    x = workloads.inputs(w)
+    send = to_slabs(rr, x, "fp32", guard=True)
+    recv = rr.allreduce_ring_staged(send.ranks, None, "sum", 1, team=1)
+    rr.allreduce_ring(send.ranks, "sum", 1, team=1)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(send, "fp32", count)
+    for r in range(R):
+        assert torch.equal(send.ranks[r].view(torch.int32), recv[r].view(torch.int32))
+    pos = sample_positions(count, R, "fp32", 1, p, 20000, 97)
+    pos = np.unique(np.concatenate([pos, (1 << 28) - 2 + np.arange(4),   # around 1 GiB into chunk 0
+                                    (p["chunk_len"] + (1 << 28)) - 2 + np.arange(4)]))
+    pos = pos[pos < count]
+    idx = torch.from_numpy(pos).cuda()
+    got = np.stack([to_host(t.index_select(0, idx), "fp32") for t in send.ranks], axis=1)
+    want = oracle_at(x, pos, "fp32", "sum")
+    assert bits_equal(got, want.view(got.dtype), "fp32").all()
