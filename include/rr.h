@@ -139,6 +139,12 @@ typedef enum {
                                          pass if some peer's witness has not advanced.
                                          A lower bound (a witness may land just before
                                          its counting add); slower, for tests only */
+#define RR_FLAG_STREAM_LOADS     0x20u /* in-place ring: mark the loads of the
+                                         predecessor's buffer non-temporal (always,
+                                         not only when the buffers exceed the
+                                         Infinity Cache; see rr_plan_t.stream_loads) */
+#define RR_FLAG_CACHED_LOADS     0x40u /* in-place ring: never mark them (both flags
+                                         together: RR_ERR_INVALID) */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -173,7 +179,13 @@ typedef struct {
     int32_t rounds;      /* lane groups each workgroup runs one after another */
     int32_t depth;       /* lanes each workgroup interleaves */
     int32_t fused;       /* 1 if the boundary hop is fused (RR_FLAG_FUSED_BOUNDARY) */
-    int32_t reserved;
+    int32_t stream_loads;/* in-place ring: 1 if the loads of the predecessor's buffer
+                            are non-temporal.  By default when the R buffers together
+                            exceed the 256 MB Infinity Cache: a chunk read from the
+                            predecessor is not read again before it is overwritten,
+                            so the hint leaves the cache to the partials each rank
+                            writes for its successor; when everything fits, it only
+                            evicts lines that would have hit. */
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */
     uint64_t sub_len;    /* elements per team member */

@@ -49,6 +49,8 @@ FLAG_NO_POINTER_CHECK = 0x2
 FLAG_COOPERATIVE = 0x4
 FLAG_FUSED_BOUNDARY = 0x8
 FLAG_AUDIT = 0x10
+FLAG_STREAM_LOADS = 0x20
+FLAG_CACHED_LOADS = 0x40
 
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16",
                  torch.float16: "fp16"}
@@ -68,7 +70,7 @@ class _Plan(ctypes.Structure):
                 ("xcd_map", ctypes.c_int32), ("cooperative", ctypes.c_int32),
                 ("resident_max", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("depth", ctypes.c_int32), ("fused", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
+                ("stream_loads", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
                 ("slice_len", ctypes.c_uint64), ("sub_len", ctypes.c_uint64),
                 ("hbm_bytes", ctypes.c_uint64)]
 
@@ -174,10 +176,14 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
+_LOADS = {"auto": 0, "stream": FLAG_STREAM_LOADS, "cached": FLAG_CACHED_LOADS}
+
+
 def _options(sync="auto", team=0, block=0, rounds=0, timeout_ns=0, inject=0, flags=0, depth=0,
-             fused=False):
+             fused=False, loads="auto"):
     if fused:
         flags |= FLAG_FUSED_BOUNDARY
+    flags |= _LOADS[loads]
     return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, rounds,
                    timeout_ns, inject, flags, depth, 0)
 

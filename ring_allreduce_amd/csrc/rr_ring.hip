@@ -49,6 +49,9 @@ constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
 // that hop risks leaving the 256 MB Infinity Cache before it is read back.
 constexpr uint64_t kRoundBytes = 192ull << 20;
 constexpr uint64_t kLongNapBytes = 64ull << 20;
+// The Infinity Cache: above this footprint the ring's loads of the
+// predecessor's buffer are non-temporal.
+constexpr uint64_t kInfinityCacheBytes = 256ull << 20;
 // Lanes a workgroup interleaves when the caller does not choose: a per-hop
 // barrier waits for the slowest of R workgroups, which a second lane hides; a
 // predecessor hand-off is cheap enough that a second lane costs more than it
@@ -80,6 +83,7 @@ struct RingArgs {
     int32_t rounds;      // lane groups each workgroup runs one after another
     int32_t depth;       // lanes each workgroup interleaves hop by hop (1..kMaxDepth)
     int32_t long_nap;    // barrier waits poll slowly (a hop moves enough data to hide it)
+    int32_t stream_in;   // loads of the predecessor's buffer are non-temporal
 };
 
 __device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -188,7 +192,20 @@ __device__ __forceinline__ void acquire_stores(bool local) {
 // XCD that L2 already holds the producer's stores, so the consumer needs no
 // cache invalidation at all.  The descriptor also bounds every load: a load
 // outside [base, base + bytes) returns zero instead of touching memory.
+//
+// When the R buffers together exceed the Infinity Cache, the in-place ring also
+// marks these loads non-temporal (nt): a partial or a finished chunk read from
+// the predecessor's buffer is not read again before it is overwritten, so its
+// lines are the first the caches should give up, which keeps the lines a rank
+// writes for its own successor cached until the next hop reads them (measured:
+// 4% at 8 ranks x 64 MiB, 12% at 64 ranks x 32 MiB in barrier mode).  When
+// everything fits, the hint only evicts lines that would have hit (up to 30%
+// slower at 16 ranks x 16 MiB), so those calls keep device scope alone.  The
+// staged loop's receive slots are rewritten every other step and lose 2-5% with
+// the hint, so they never use it.
 constexpr int kAuxDeviceScope = 16;             // sc1
+constexpr int kAuxNonTemporal = 2;              // nt
+constexpr int kAuxRingIncoming = kAuxDeviceScope | kAuxNonTemporal;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw (untyped) buffer access on gfx9
 constexpr uint64_t kPieceBytes = 1ull << 30;    // one descriptor covers at most this
 
@@ -197,15 +214,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t incoming(const void* base, uin
                                              (int)kBufferWord3);
 }
 
+template <int AUX = kAuxDeviceScope>
 __device__ __forceinline__ u32x4 load_in(__amdgpu_buffer_rsrc_t rs, uint32_t vec) {
     return __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(vec * 16u), 0, kAuxDeviceScope));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(vec * 16u), 0, AUX));
 }
 
 // One hop of one workgroup over elements [lo, hi) of both buffers.  ReduceScatter:
 // dst = fold(src, dst).  AllGather: dst = src, bit for bit.  16-byte vectors,
 // U vectors per thread in flight, then a scalar tail (only at the ragged end).
-template <int DT, int OP, int BLOCK, int U>
+template <int DT, int OP, int BLOCK, int U, int AUX>
 __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void* dstbuf,
                                           void* dst2buf, uint64_t lo, uint64_t hi) {
     constexpr int ES = ElemBytes<DT>::value;
@@ -223,7 +241,7 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
 #pragma unroll
             for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
 #pragma unroll
@@ -234,7 +252,7 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
             }
         }
         for (; i < nv; i += BLOCK) {
-            const u32x4 v = fold4<DT, OP>(load_in(rs, i), d[i]);
+            const u32x4 v = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
             d[i] = v;
             d2[i] = v;
         }
@@ -242,23 +260,23 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
 #pragma unroll
             for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
 #pragma unroll
             for (int u = 0; u < U; ++u) d[i + u * BLOCK] = fold4<DT, OP>(x[u], y[u]);
         }
-        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(load_in(rs, i), d[i]);
+        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
     } else {
         constexpr int UC = 2 * U;
         for (; i + (UC - 1) * BLOCK < nv; i += UC * BLOCK) {
             u32x4 x[UC];
 #pragma unroll
-            for (int u = 0; u < UC; ++u) x[u] = load_in(rs, i + u * BLOCK);
+            for (int u = 0; u < UC; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
 #pragma unroll
             for (int u = 0; u < UC; ++u) d[i + u * BLOCK] = x[u];
         }
-        for (; i < nv; i += BLOCK) d[i] = load_in(rs, i);
+        for (; i < nv; i += BLOCK) d[i] = load_in<AUX>(rs, i);
     }
     const uint64_t t = (uint64_t)nv * V + threadIdx.x;  // fewer than V elements remain
     if (t < n) {
@@ -267,13 +285,13 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
         char* dp2 = dst2buf ? (char*)dst2buf + (lo + t) * ES : nullptr;
         if constexpr (ES == 2) {
             const uint16_t in =
-                __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kAuxDeviceScope);
+                __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, AUX);
             const uint16_t v =
                 reduce ? (uint16_t)Fold<DT, OP>::half(in, *(const uint16_t*)dp) : in;
             *(uint16_t*)dp = v;
             if (dp2) *(uint16_t*)dp2 = v;
         } else {
-            const uint32_t in = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kAuxDeviceScope);
+            const uint32_t in = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, AUX);
             const uint32_t v = reduce ? Fold<DT, OP>::lane(in, *(const uint32_t*)dp) : in;
             *(uint32_t*)dp = v;
             if (dp2) *(uint32_t*)dp2 = v;
@@ -282,11 +300,16 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
 }
 
 template <int DT, int OP, int BLOCK, int U>
-__device__ __forceinline__ void hop_body(bool reduce, const void* srcbuf, void* dstbuf,
-                                         void* dst2buf, uint64_t lo, uint64_t hi) {
+__device__ __forceinline__ void hop_body(bool reduce, bool stream, const void* srcbuf,
+                                         void* dstbuf, void* dst2buf, uint64_t lo, uint64_t hi) {
     constexpr uint64_t kPiece = kPieceBytes / ElemBytes<DT>::value;  // elements, vector multiple
-    for (uint64_t p = lo; p < hi; p += kPiece)
-        hop_piece<DT, OP, BLOCK, U>(reduce, srcbuf, dstbuf, dst2buf, p, umin(p + kPiece, hi));
+    for (uint64_t p = lo; p < hi; p += kPiece) {
+        const uint64_t q = umin(p + kPiece, hi);
+        if (stream)
+            hop_piece<DT, OP, BLOCK, U, kAuxRingIncoming>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+        else
+            hop_piece<DT, OP, BLOCK, U, kAuxDeviceScope>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+    }
 }
 
 template <int DT, int OP, int BLOCK>
@@ -385,7 +408,8 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
                 const uint64_t lo = base + off_lo[p];
                 const uint64_t hi = umin(base + off_hi[p], a.count);
                 if (lo < hi && !skip)
-                    hop_body<DT, OP, BLOCK, U>(reduce, a.bufs[r], a.bufs[succ], dst2, lo, hi);
+                    hop_body<DT, OP, BLOCK, U>(reduce, a.stream_in != 0, a.bufs[r], a.bufs[succ],
+                                               dst2, lo, hi);
 
                 if (g < a.g_last) {
                     if (!decided) {
@@ -496,6 +520,8 @@ struct StagedArgs {
 
 // One step's data over n elements: in (the receive slot, device-scope loads),
 // local (the rank's input), out (its output), next (the successor's slot).
+// Output stores are non-temporal: nothing in the collective reads them back,
+// while the successor reads `next` one step later (measured: 1-3% at 8 ranks).
 template <int DT, int OP, int BLOCK, int P>
 __device__ __forceinline__ void staged_piece(const void* in, const void* local, void* out,
                                              void* next, uint64_t n, bool aligned) {
@@ -528,7 +554,7 @@ __device__ __forceinline__ void staged_piece(const void* in, const void* local, 
                 if constexpr (Q::reduce) v = fold4<DT, OP>(x[u], y[u]);
                 else if constexpr (Q::in) v = x[u];
                 else v = y[u];
-                if constexpr (Q::out) op[i + u * BLOCK] = v;
+                if constexpr (Q::out) __builtin_nontemporal_store(v, &op[i + u * BLOCK]);
                 if constexpr (Q::send) np[i + u * BLOCK] = v;
             }
         }
@@ -537,7 +563,7 @@ __device__ __forceinline__ void staged_piece(const void* in, const void* local, 
             if constexpr (Q::reduce) v = fold4<DT, OP>(load_in(rs, i), lp[i]);
             else if constexpr (Q::in) v = load_in(rs, i);
             else v = lp[i];
-            if constexpr (Q::out) op[i] = v;
+            if constexpr (Q::out) __builtin_nontemporal_store(v, &op[i]);
             if constexpr (Q::send) np[i] = v;
         }
         done = (uint64_t)nv * V;
@@ -729,7 +755,8 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
 // arrivals per call (R with one part).  The waiter advances a persisted shadow
 // (the article's per-signal shadows) instead of reading the signal at entry,
 // which is why no entry barrier is needed here: there is no base value to race
-// with.
+// with.  Loads and stores are both non-temporal: each byte crosses once and the
+// call never reads a receive buffer.
 struct A2AArgs {
     const void* send[kMaxDevices];
     void* recv[kMaxDevices];
@@ -774,9 +801,9 @@ __global__ void __launch_bounds__(BLOCK) alltoall_kernel(const A2AArgs a) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(&s4[v + u * BLOCK]);
 #pragma unroll
-                for (int u = 0; u < U; ++u) d4[v + u * BLOCK] = x[u];
+                for (int u = 0; u < U; ++u) __builtin_nontemporal_store(x[u], &d4[v + u * BLOCK]);
             }
-            for (; v < nv; v += BLOCK) d4[v] = __builtin_nontemporal_load(&s4[v]);
+            for (; v < nv; v += BLOCK) __builtin_nontemporal_store(__builtin_nontemporal_load(&s4[v]), &d4[v]);
             done = nv * V;
         }
         for (uint64_t t = done + threadIdx.x; t < n; t += BLOCK) {
@@ -1045,6 +1072,7 @@ DeviceState g_dev[kMaxDevices];
 
 struct Plan {
     int long_nap;
+    int stream_in;
     int fuse;
     int sync;
     int team;
@@ -1238,6 +1266,7 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     const int block = opt && opt->block ? opt->block : 512;
     const int requested = opt ? opt->sync : RR_SYNC_AUTO;
     const uint32_t flags = opt ? opt->flags : 0;
+    if ((flags & RR_FLAG_STREAM_LOADS) && (flags & RR_FLAG_CACHED_LOADS)) return RR_ERR_INVALID;
     p->block = block;
     p->chunk_len = round_up(ceil_div(count, (uint64_t)R), V);
     p->slice_len = round_up(ceil_div(p->chunk_len, (uint64_t)nslices), V);
@@ -1353,6 +1382,8 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     // all ranks (about 10 us of traffic, so a later wake-up of up to ~2 us is
     // hidden; smaller buffers are latency-bound and keep the fast poll)
     p->long_nap = sync == RR_SYNC_BARRIER && 3ull * count * elem_bytes(dt) >= kLongNapBytes;
+    p->stream_in = (flags & RR_FLAG_STREAM_LOADS) ||
+                   (!(flags & RR_FLAG_CACHED_LOADS) && (uint64_t)R * nbytes > kInfinityCacheBytes);
     return RR_OK;
 }
 
@@ -1391,6 +1422,7 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.depth = p.depth;
     a.fuse = p.fuse;
     a.long_nap = p.long_nap;
+    a.stream_in = p.stream_in;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
     RingKernel k = pick_ring_kernel(dt, op, p.block);
@@ -1435,6 +1467,7 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     if (requested == RR_SYNC_BARRIER) return RR_ERR_UNSUPPORTED;  // credits pace the loop
     p->block = kStagedBlock;
     p->fuse = 0;
+    p->stream_in = 0;
     p->chunk_len = mode == MODE_ALLREDUCE ? round_up(ceil_div(n, (uint64_t)R), V) : n;
     p->slice_len = round_up(ceil_div(p->chunk_len, (uint64_t)nslices), V);
     p->g_first = 0;
@@ -1641,6 +1674,7 @@ static rr_status_t make_a2a_plan(const DeviceState* d, int R, uint64_t count, in
     p->rounds = 1;
     p->depth = 1;
     p->fuse = 0;
+    p->stream_in = 0;
     p->chunk_len = count;
     p->slice_len = count;
     p->sub_len = round_up(ceil_div(count, (uint64_t)parts), V);
@@ -1809,6 +1843,7 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
     out->rounds = p.rounds;
     out->depth = p.depth;
     out->fused = p.fuse;
+    out->stream_loads = p.stream_in;
     out->block = p.block;
     out->grid = p.grid;
     out->launches = (R == 1 || count == 0) ? 0 : p.launches;

@@ -73,6 +73,36 @@ def test_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"R={R} count={count}")
 
 
+# ------------------------------------- load policy (non-temporal incoming loads)
+
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("bf16", "max")])
+@pytest.mark.parametrize("R,count,nslices,team", [SMALL[0], SMALL[3], SMALL[5], SMALL[7]])
+@pytest.mark.parametrize("sync", ["p2p", "barrier", "launch"])
+def test_stream_loads_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
+    """Small buffers take cached loads by default; forcing the non-temporal hint
+    runs the other instantiation of every hop over the same ragged cases."""
+    log(f"case stream loads {dtype} {op} R={R} count={count} ns={nslices} team={team} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], R * 31 + count % 97)
+    want = oracle_expect(x, op)
+    for opts in (dict(loads="stream"), dict(loads="stream", fused=True)):
+        got = run_case(rr, x, dtype, op, nslices, sync=sync, team=team, **opts)
+        assert_matches_oracle(got, want, dtype, f"R={R} count={count} {opts}")
+
+
+def test_stream_loads_plan(rr):
+    """Default: non-temporal once the R buffers exceed the 256 MB Infinity Cache."""
+    assert rr.plan(8, 16 << 20, "fp32", 4)["stream_loads"] == 1        # 512 MiB
+    assert rr.plan(16, 4 << 20, "fp32", 4)["stream_loads"] == 0        # 256 MiB: fits
+    assert rr.plan(16, (4 << 20) + 4, "fp32", 4)["stream_loads"] == 1
+    assert rr.plan(8, 16 << 20, "bf16", 4)["stream_loads"] == 0        # 256 MiB
+    assert rr.plan(16, 1 << 10, "fp32", 4, loads="stream")["stream_loads"] == 1
+    assert rr.plan(8, 16 << 20, "fp32", 4, loads="cached")["stream_loads"] == 0
+    for phase in ("allreduce_staged", "reduce_scatter_blocks", "all_gather_blocks", "alltoall"):
+        assert rr.plan(8, 16 << 20, "fp32", 1, phase=phase)["stream_loads"] == 0
+    with pytest.raises(rr.RRError):
+        rr.plan(8, 1024, "fp32", 1, flags=rr.FLAG_STREAM_LOADS | rr.FLAG_CACHED_LOADS)
+
+
 # ----------------------------------------------- several tiles, default plan
 
 MULTI = [(8, "fp32", "sum", (1 << 20) + 13, 4), (8, "bf16", "sum", (1 << 21) + 9, 8),
@@ -88,6 +118,14 @@ def test_multi_tile(rr, R, dtype, op, count, nslices, sync):
     x = workloads.generate(R, count, dtype, DIST[dtype], 100 + R)
     got = run_case(rr, x, dtype, op, nslices, sync=sync)
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"multi R={R}")
+
+
+@pytest.mark.parametrize("R,dtype,op,count,nslices", MULTI)
+def test_multi_tile_stream_loads(rr, R, dtype, op, count, nslices):
+    log(f"case multi stream R={R} {dtype} {op} count={count} ns={nslices}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], 100 + R)
+    got = run_case(rr, x, dtype, op, nslices, sync="barrier", loads="stream")
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"multi stream R={R}")
 
 
 @pytest.mark.parametrize("rounds,depth", [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2),
@@ -382,6 +420,16 @@ def test_full_r64_fp32_32MiB(rr):
                          ids=lambda w: w.name)
 def test_full_fused_boundary(rr, w):
     _full_size(rr, w, 5000, dict(fused=True))
+
+
+def test_full_cached_loads(rr):
+    """The default workload with the hint forced off (its default is on)."""
+    _full_size(rr, workloads.R8_FP32_64MIB, 5000, dict(loads="cached"))
+
+
+def test_full_stream_loads_in_cache(rr):
+    """16 ranks x 16 MiB fit the Infinity Cache (default off); forced on."""
+    _full_size(rr, workloads.r16_sweep(6, "sum", 4), 5000, dict(loads="stream"))
 
 
 @pytest.mark.parametrize("k", range(0, 9))
