@@ -330,6 +330,7 @@ def main():
         "config": {"workload": w.name, "path": path, "R": w.R, "bytes_per_rank": w.bytes_per_rank,
                    "op": w.op, "nslices": w.nslices, "sync": p["sync"], "team": p["team"],
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
+                   "rounds": p["rounds"], "depth": p["depth"], "stream_loads": p["stream_loads"],
                    "fused_boundary": bool(p["fused"]) if path == "ring" else False,
                    "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
         "timing": timing,

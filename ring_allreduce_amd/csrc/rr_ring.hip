@@ -45,9 +45,17 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxDepth = 4;
 constexpr int kSlots = RR_MAX_SLICES * RR_MAX_RANKS;  // (context, rank) pairs
 constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
-// Bytes one hop of the lanes in flight may move before a partial written in
-// that hop risks leaving the 256 MB Infinity Cache before it is read back.
-constexpr uint64_t kRoundBytes = 192ull << 20;
+// Bytes one hop of the lanes in flight may move (3 N / rounds over all ranks):
+// fewer keep a partial cached until the next hop reads it, more save hand-offs.
+// Fitted on MI355X over R = 2..64 and 512 MiB..4 GiB in all: max(96 MiB,
+// 12 MiB x R) with predecessor hand-offs, twice that with a barrier per hop,
+// which waits for all R ranks of a lane and so prefers fewer, larger rounds
+// (mean 0.4% and 0.8% slower than the best power-of-two rounds of each case).
+constexpr uint64_t kRoundBytesMin = 96ull << 20;
+constexpr uint64_t kRoundBytesPerRank = 12ull << 20;
+// The staged loop's step budget (its partials and messages stay in the
+// Infinity Cache between steps).
+constexpr uint64_t kRoundBytesStaged = 192ull << 20;
 constexpr uint64_t kLongNapBytes = 64ull << 20;
 // The Infinity Cache: above this footprint the ring's loads of the
 // predecessor's buffer are non-temporal.
@@ -1198,20 +1206,36 @@ static bool valid_dtype(int dt) {
 static bool valid_op(int op) { return op == RR_SUM || op == RR_MAX || op == RR_MIN || op == RR_PROD; }
 
 // Argument checks that need no device.
+// Option and size limits of each call family (phase numbering of
+// rr_plan_query), shared by the calls and the plan query so that both reject
+// the same arguments.
+static rr_status_t check_shape(int R, uint64_t count, int phase, const rr_options_t* opt) {
+    if (R < 1 || R > RR_MAX_RANKS) return RR_ERR_INVALID;
+    const uint64_t kMaxElems = (uint64_t)1 << 40;
+    if (phase <= 2) {
+        if (count > kMaxElems) return RR_ERR_INVALID;
+    } else if (count > kMaxElems || (uint64_t)R * count > kMaxElems) {
+        return RR_ERR_INVALID;
+    }
+    if (!opt) return RR_OK;
+    const int max_sync = phase == 6 ? RR_SYNC_P2P : RR_SYNC_LAUNCH;
+    if (opt->sync < RR_SYNC_AUTO || opt->sync > max_sync) return RR_ERR_INVALID;
+    if (opt->team < 0 || opt->team > (phase == 6 ? 65536 : 4096)) return RR_ERR_INVALID;
+    if (phase == 6) return RR_OK;
+    if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
+    if (phase <= 2 && (opt->depth < 0 || opt->depth > kMaxDepth)) return RR_ERR_INVALID;
+    if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
+        return RR_ERR_INVALID;
+    return RR_OK;
+}
+
 static rr_status_t check_args(void* const* bufs, int R, size_t count, int dt, int op, int nslices,
                               const rr_options_t* opt) {
     if (R < 1 || R > RR_MAX_RANKS) return RR_ERR_INVALID;
     if (nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
     if (!valid_dtype(dt) || !valid_op(op)) return RR_ERR_INVALID;
-    if (count > (size_t)1 << 40) return RR_ERR_INVALID;
-    if (opt) {
-        if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
-        if (opt->team < 0 || opt->team > 4096) return RR_ERR_INVALID;
-        if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
-        if (opt->depth < 0 || opt->depth > kMaxDepth) return RR_ERR_INVALID;
-        if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
-            return RR_ERR_INVALID;
-    }
+    const rr_status_t st = check_shape(R, count, 0, opt);
+    if (st != RR_OK) return st;
     if (!bufs) return RR_ERR_INVALID;
     if (R == 1 || count == 0) return RR_OK;
     const size_t bytes = count * elem_bytes(dt);
@@ -1293,9 +1317,9 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
 
     // Workgroups per rank (cols): about 16 waves per CU, two 512-thread
     // workgroups.  Each interleaves `depth` lanes and runs `rounds` groups of
-    // them one after another; rounds are chosen so that one hop of the lanes in
-    // flight (3 N / rounds bytes over all ranks) stays within the Infinity Cache,
-    // so a partial is still cached when the next hop reads it.
+    // them one after another; rounds bound one hop of the lanes in flight
+    // (3 N / rounds bytes over all ranks), so that a partial is still cached
+    // when the next hop reads it.
     const int target_cols = std::max(1, d->cus * 16 * 64 / block / R);
     const bool fixed_depth = opt && opt->depth > 0;
     const bool fixed_rounds = opt && opt->rounds > 0;
@@ -1306,7 +1330,12 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
         rounds = opt->rounds;
     } else {
         const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
-        rounds = (int)std::max<uint64_t>(1, ceil_div(hop_bytes, kRoundBytes));
+        const uint64_t per_round =
+            std::max<uint64_t>(kRoundBytesMin, (uint64_t)R * kRoundBytesPerRank) *
+            (requested == RR_SYNC_BARRIER ? 2 : 1);
+        uint64_t k = 1;  // a power of two: lanes split evenly over the XCDs
+        while (k * per_round < hop_bytes) k *= 2;
+        rounds = (int)k;
     }
     int team;
     const uint64_t slice_vecs = p->slice_len / V;
@@ -1480,10 +1509,10 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     p->resident_max = resident_limit(d, kernel, kStagedBlock);
     const int target_cols = std::max(1, d->cus * 16 * 64 / kStagedBlock / R);
     // rounds: one step of the lanes in flight (reads and writes of about three
-    // chunks per rank) within the Infinity Cache budget, as for the ring
+    // chunks per rank) within kRoundBytesStaged
     const uint64_t step_bytes = 3ull * (uint64_t)R * p->chunk_len * es;
     int rounds = opt && opt->rounds > 0 ? opt->rounds
-                                        : (int)std::max<uint64_t>(1, ceil_div(step_bytes, kRoundBytes));
+                                        : (int)std::max<uint64_t>(1, ceil_div(step_bytes, kRoundBytesStaged));
     int team;
     if (opt && opt->team > 0) {
         team = opt->team;
@@ -1527,14 +1556,8 @@ static rr_status_t check_staged_args(const void* const* send, void* const* recv,
                                      int dt, int op, int nslices, int mode, const rr_options_t* opt) {
     if (R < 1 || R > RR_MAX_RANKS || nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
     if (!valid_dtype(dt) || !valid_op(op)) return RR_ERR_INVALID;
-    if (n > (uint64_t)1 << 40 || (uint64_t)R * n > (uint64_t)1 << 40) return RR_ERR_INVALID;
-    if (opt) {
-        if (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_LAUNCH) return RR_ERR_INVALID;
-        if (opt->team < 0 || opt->team > 4096) return RR_ERR_INVALID;
-        if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
-        if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
-            return RR_ERR_INVALID;
-    }
+    const rr_status_t st = check_shape(R, n, 3 + mode, opt);
+    if (st != RR_OK) return st;
     if (!send || !recv) return RR_ERR_INVALID;
     if (n == 0) return RR_OK;
     const uint64_t es = elem_bytes(dt);
@@ -1692,9 +1715,8 @@ static rr_status_t make_a2a_plan(const DeviceState* d, int R, uint64_t count, in
 static rr_status_t run_alltoall(const void* const* send, void* const* recv, int R, uint64_t count,
                                 int dt, const rr_options_t* opt, rr_stream_t stream) {
     if (R < 1 || R > RR_MAX_RANKS || !valid_dtype(dt)) return RR_ERR_INVALID;
-    if ((uint64_t)R * count > (uint64_t)1 << 40) return RR_ERR_INVALID;
-    if (opt && (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_P2P)) return RR_ERR_INVALID;
-    if (opt && (opt->team < 0 || opt->team > 65536)) return RR_ERR_INVALID;
+    rr_status_t st0 = check_shape(R, count, 6, opt);
+    if (st0 != RR_OK) return st0;
     if (!send || !recv) return RR_ERR_INVALID;
     if (count == 0) return RR_OK;
     const uint64_t es = elem_bytes(dt);
@@ -1827,8 +1849,10 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
     if (!out || phase < 0 || phase > 6) return RR_ERR_INVALID;
     if (R < 1 || R > RR_MAX_RANKS || nslices < 1 || nslices > RR_MAX_SLICES) return RR_ERR_INVALID;
     if (!valid_dtype(dt)) return RR_ERR_INVALID;
+    rr_status_t st = check_shape(R, count, phase, opt);
+    if (st != RR_OK) return st;
     DeviceState* d = nullptr;
-    rr_status_t st = ensure_device(&d);
+    st = ensure_device(&d);
     if (st != RR_OK) return st;
     Plan p;
     if (phase <= 2)

@@ -183,3 +183,24 @@ def test_product_path_has_no_oracle_dependency():
                 assert "oracle" not in text.lower(), f
     out = subprocess.run(["ldd", os.path.join(pkg, "librr.so")], capture_output=True, text=True).stdout
     assert "ring_oracle" not in out
+
+
+@pytest.mark.parametrize("phase,opts", [
+    (0, dict(team=4097)), (0, dict(rounds=5000)), (0, dict(depth=5)), (0, dict(block=128)),
+    (0, dict(sync=4)), (2, dict(team=-1)), (3, dict(team=4097)), (4, dict(rounds=-1)),
+    (5, dict(block=96)), (6, dict(sync=2)), (6, dict(team=65537)),
+])
+def test_plan_query_rejects_what_the_call_rejects(rr, phase, opts):
+    """The plan query checks options and sizes as the calls do, before any
+    device work (so the same argument never passes one and fails the other)."""
+    p = rr._Plan()
+    o = rr._options(**opts)
+    assert rr._plan_query(4, 1 << 20, 1, 1, phase, ctypes.byref(o), ctypes.byref(p)) == \
+        rr.RR_ERR_INVALID
+
+
+@pytest.mark.parametrize("phase", [3, 4, 5, 6])
+def test_plan_query_rejects_oversized_block_sets(rr, phase):
+    p = rr._Plan()
+    assert rr._plan_query(8, (1 << 40) // 4, 1, 1, phase, None, ctypes.byref(p)) == \
+        rr.RR_ERR_INVALID
