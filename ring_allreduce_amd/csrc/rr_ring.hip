@@ -53,9 +53,15 @@ constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
 // (mean 0.4% and 0.8% slower than the best power-of-two rounds of each case).
 constexpr uint64_t kRoundBytesMin = 96ull << 20;
 constexpr uint64_t kRoundBytesPerRank = 12ull << 20;
-// The staged loop's step budget (its partials and messages stay in the
-// Infinity Cache between steps).
-constexpr uint64_t kRoundBytesStaged = 192ull << 20;
+// The staged loop bounds one step of the lanes in flight the same way: 192 MiB
+// for its AllReduce and ReduceScatter (a sweep of R = 2..64, 512 MiB..4 GiB:
+// 1.2% and 0.5% from the best power-of-two rounds on average).  Its AllGather
+// only forwards data, and its hand-offs stay in the L2s when a step moves
+// max(48 MiB, 384 MiB / R) over all ranks (2.2% from the best on average, against
+// 7% with 192 MiB; 9% faster at 8 ranks x 64 MiB, 15% at 64 ranks x 32 MiB).
+constexpr uint64_t kStagedRoundBytes = 192ull << 20;
+constexpr uint64_t kGatherRoundMin = 48ull << 20;
+constexpr uint64_t kGatherRoundSpan = 384ull << 20;
 constexpr uint64_t kLongNapBytes = 64ull << 20;
 // The Infinity Cache: above this footprint the ring's loads of the
 // predecessor's buffer are non-temporal.
@@ -1508,11 +1514,15 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     if (!kernel) return RR_ERR_INVALID;
     p->resident_max = resident_limit(d, kernel, kStagedBlock);
     const int target_cols = std::max(1, d->cus * 16 * 64 / kStagedBlock / R);
-    // rounds: one step of the lanes in flight (reads and writes of about three
-    // chunks per rank) within kRoundBytesStaged
+    // rounds (a power of two): one step of the lanes in flight (reads and
+    // writes of about three chunks per rank) within the step budget
     const uint64_t step_bytes = 3ull * (uint64_t)R * p->chunk_len * es;
-    int rounds = opt && opt->rounds > 0 ? opt->rounds
-                                        : (int)std::max<uint64_t>(1, ceil_div(step_bytes, kRoundBytesStaged));
+    const uint64_t budget =
+        mode == MODE_AG ? std::max<uint64_t>(kGatherRoundMin, kGatherRoundSpan / (uint64_t)R)
+                        : kStagedRoundBytes;
+    uint64_t k = 1;
+    while (k * budget < step_bytes) k *= 2;
+    int rounds = opt && opt->rounds > 0 ? opt->rounds : (int)k;
     int team;
     if (opt && opt->team > 0) {
         team = opt->team;
