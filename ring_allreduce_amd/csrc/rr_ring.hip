@@ -489,8 +489,14 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
 //                   (r - k) mod R.
 constexpr int kFifoSlots = 2;
 constexpr int kStagedBlock = 512;
-constexpr int kA2ABlock = 256;
-constexpr int kA2AWavesPerCU = 4;
+// AlltoAll: one 1024-thread workgroup per CU, 4 vectors per thread in flight
+// (against 256 threads x 8: +3% at 8 ranks x 64 MiB fp32, +9% bf16 256 MiB, +4%
+// at 64 ranks)
+constexpr int kA2ABlock = 1024;
+constexpr int kA2AUnroll = 4;
+constexpr int kCopyBlock = 512;
+constexpr int kCopyPerCU = 4;
+constexpr int kA2AWavesPerCU = 16;
 enum : int { MODE_ALLREDUCE = 0, MODE_RS = 1, MODE_AG = 2 };
 enum : int { P_SEND = 0, P_RRS = 1, P_RRCS = 2, P_RCS = 3, P_RECV = 4, P_RRC = 5, P_CS = 6 };
 
@@ -789,7 +795,7 @@ struct A2AArgs {
 template <int ES, int BLOCK>
 __global__ void __launch_bounds__(BLOCK) alltoall_kernel(const A2AArgs a) {
     constexpr int V = 16 / ES;
-    constexpr int U = 8;
+    constexpr int U = kA2AUnroll;
     const int R = a.R;
     const int r = (int)blockIdx.x / a.parts;
     const int part = (int)blockIdx.x - r * a.parts;
@@ -1042,24 +1048,28 @@ __global__ void __launch_bounds__(256) fill_u64_kernel(uint64_t* p, uint64_t n, 
 
 // Streaming copy: the bandwidth reference for the ring kernels.  Each
 // workgroup copies one contiguous span (DRAM pages stay open longer than with a
-// grid-wide stride); nontemporal hints, as the data are touched once.
-__global__ void __launch_bounds__(256) copy_kernel(const u32x4* __restrict__ src,
-                                                   u32x4* __restrict__ dst, uint64_t nvec,
-                                                   const uint8_t* __restrict__ src_tail,
-                                                   uint8_t* __restrict__ dst_tail, uint32_t ntail) {
+// grid-wide stride); nontemporal hints, as the data are touched once.  512
+// threads x 8 vectors in flight, 4 workgroups per CU: 5.9 TB/s on MI355X, where
+// 256-thread workgroups reach 5.6 at any grid size.
+__global__ void __launch_bounds__(kCopyBlock) copy_kernel(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ dst, uint64_t nvec,
+                                                          const uint8_t* __restrict__ src_tail,
+                                                          uint8_t* __restrict__ dst_tail,
+                                                          uint32_t ntail) {
     constexpr int U = 8;
+    constexpr int B = kCopyBlock;
     const uint64_t per = (nvec + gridDim.x - 1) / gridDim.x;
     const uint64_t lo = (uint64_t)blockIdx.x * per;
     const uint64_t hi = lo + per < nvec ? lo + per : nvec;
     uint64_t i = lo + threadIdx.x;
-    for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    for (; i + (U - 1) * B < hi; i += U * B) {
         u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(&src[i + u * 256]);
+        for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(&src[i + u * B]);
 #pragma unroll
-        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(x[u], &dst[i + u * 256]);
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(x[u], &dst[i + u * B]);
     }
-    for (; i < hi; i += 256) dst[i] = src[i];
+    for (; i < hi; i += B) dst[i] = src[i];
     if (blockIdx.x == 0 && threadIdx.x < ntail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
@@ -1608,8 +1618,8 @@ static rr_status_t copy_bytes(void* dst, const void* src, uint64_t bytes, const 
     const uint64_t nvec = bytes / 16;
     const uint32_t ntail = (uint32_t)(bytes % 16);
     const unsigned grid = (unsigned)std::max<uint64_t>(
-        1, std::min<uint64_t>((uint64_t)d->cus * 16, ceil_div(nvec, 2048)));
-    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst,
+        1, std::min<uint64_t>((uint64_t)d->cus * kCopyPerCU, ceil_div(nvec, 8 * kCopyBlock)));
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kCopyBlock), 0, s, (const u32x4*)src, (u32x4*)dst,
                        nvec, (const uint8_t*)src + nvec * 16, (uint8_t*)dst + nvec * 16, ntail);
     return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
 }
@@ -1696,7 +1706,7 @@ static rr_status_t make_a2a_plan(const DeviceState* d, int R, uint64_t count, in
     p->resident_max = resident_limit(d, kernel, kA2ABlock);
     // parts per block: about kA2AWavesPerCU waves per CU in all, every
     // workgroup resident (the receiving workgroups wait for the others)
-    const uint64_t by_size = std::max<uint64_t>(1, count / V / ((uint64_t)kA2ABlock * 8));
+    const uint64_t by_size = std::max<uint64_t>(1, count / V / ((uint64_t)kA2ABlock * kA2AUnroll));
     const uint64_t wanted = std::max<uint64_t>(
         1, std::min<uint64_t>((uint64_t)d->cus * kA2AWavesPerCU * 64 / kA2ABlock,
                               (uint64_t)p->resident_max) / (uint64_t)R);
@@ -2103,8 +2113,8 @@ rr_status_t rr_hbm_copy(void* dst, const void* src, size_t bytes, rr_stream_t st
     const uint64_t nvec = bytes / 16;
     const uint32_t ntail = (uint32_t)(bytes % 16);
     const unsigned grid = (unsigned)std::max<uint64_t>(
-        1, std::min<uint64_t>((uint64_t)d->cus * 16, ceil_div(nvec, 2048)));
-    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+        1, std::min<uint64_t>((uint64_t)d->cus * kCopyPerCU, ceil_div(nvec, 8 * kCopyBlock)));
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kCopyBlock), 0, (hipStream_t)stream,
                        (const u32x4*)src, (u32x4*)dst, nvec, (const uint8_t*)src + nvec * 16,
                        (uint8_t*)dst + nvec * 16, ntail);
     return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
