@@ -204,3 +204,13 @@ def test_plan_query_rejects_oversized_block_sets(rr, phase):
     p = rr._Plan()
     assert rr._plan_query(8, (1 << 40) // 4, 1, 1, phase, None, ctypes.byref(p)) == \
         rr.RR_ERR_INVALID
+
+
+def test_build_script_loads_without_the_library():
+    """build() must work in a fresh checkout, where librr.so does not exist yet:
+    it loads the build script by path, without running the package's __init__
+    (which refuses to import until the library is built)."""
+    code = ("import sys, __graft_entry__ as g; m = g._load_build_script(); "
+            "assert callable(m.build) and m.LIB.endswith('librr.so'); "
+            "assert 'ring_allreduce_amd' not in sys.modules")
+    subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, check=True)
