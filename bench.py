@@ -437,7 +437,9 @@ def r16_sweep(rr, torch, np):
                                   "GB/s": round(B / ms / 1e6, 1),
                                   "pct_of_peak": round(100 * B / ms / 1e6 / HBM_PEAK_GBS, 2),
                                   "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],
-                                  "grid": p["grid"], "launches": p["launches"]}), flush=True)
+                                  "block": p["block"], "grid": p["grid"],
+                                  "stream_loads": p["stream_loads"], "launches": p["launches"]}),
+                      flush=True)
         del slabs, pristine
         torch.cuda.empty_cache()
     return 0

@@ -154,7 +154,10 @@ typedef enum {
 typedef struct {
     int32_t sync;        /* rr_sync_t */
     int32_t team;        /* workgroups per (rank, slice); 0 = choose */
-    int32_t block;       /* threads per workgroup: 0 (= 512), 256, 512 or 1024 */
+    int32_t block;       /* threads per workgroup: 128, 256, 512 or 1024; 0 = automatic:
+                            512, or 128 when R >= 16, the R buffers together exceed
+                            256 MiB and a lane's piece of a chunk is at most 64 KiB
+                            (columns are planned for 512 either way) */
     int32_t rounds;      /* lane groups each workgroup runs one after another
                             (depth * rounds must divide slices * team);
                             0 = choose from the buffer size */

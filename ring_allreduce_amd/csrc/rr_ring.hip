@@ -72,6 +72,19 @@ constexpr uint64_t kInfinityCacheBytes = 256ull << 20;
 // hides (measured on MI355X).
 constexpr int kAutoDepthBarrier = 2;
 constexpr int kAutoDepthP2P = 1;
+// Workgroup size when the caller does not choose.  Columns are planned for
+// 512-thread workgroups (two per CU); a long ring (16 ranks or more) over
+// buffers larger than the Infinity Cache whose lane pieces are at most 64 KiB
+// then runs them with 128 threads.  A workgroup's hop ends when its slowest
+// wave's stores have drained, and along a long chain of hand-offs those tails
+// add up; a shorter ring streams better with 512 threads.  Measured on MI355X,
+// same columns: 16-64 ranks x 8-64 MiB, 2-15% faster with 128 threads; 4-8
+// ranks, pieces of 128 KiB and more, or buffers that fit the cache (16 ranks x
+// 16 MiB: 6% slower in barrier mode), even or slower.
+constexpr int kAutoBlock = 512;
+constexpr int kLongRingBlock = 128;
+constexpr int kLongRingRanks = 16;
+constexpr uint64_t kLongRingPieceBytes = 64ull << 10;
 
 struct RingArgs {
     void* bufs[RR_MAX_RANKS];
@@ -1165,6 +1178,7 @@ typedef void (*RingKernel)(RingArgs);
 template <int DT, int OP>
 static RingKernel ring_kernel_for_block(int block) {
     switch (block) {
+        case 128: return ring_kernel<DT, OP, 128>;
         case 256: return ring_kernel<DT, OP, 256>;
         case 512: return ring_kernel<DT, OP, 512>;
         case 1024: return ring_kernel<DT, OP, 1024>;
@@ -1240,7 +1254,8 @@ static rr_status_t check_shape(int R, uint64_t count, int phase, const rr_option
     if (phase == 6) return RR_OK;
     if (opt->rounds < 0 || opt->rounds > 4096) return RR_ERR_INVALID;
     if (phase <= 2 && (opt->depth < 0 || opt->depth > kMaxDepth)) return RR_ERR_INVALID;
-    if (opt->block != 0 && opt->block != 256 && opt->block != 512 && opt->block != 1024)
+    if (opt->block != 0 && opt->block != 128 && opt->block != 256 && opt->block != 512 &&
+        opt->block != 1024)
         return RR_ERR_INVALID;
     return RR_OK;
 }
@@ -1303,11 +1318,11 @@ static int resident_limit(const DeviceState* d, const void* kernel, int block) {
 static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, int op,
                              int nslices, int phase, const rr_options_t* opt, Plan* p) {
     const uint64_t V = 16 / elem_bytes(dt);
-    const int block = opt && opt->block ? opt->block : 512;
+    const bool fixed_block = opt && opt->block;
+    int block = fixed_block ? opt->block : kAutoBlock;
     const int requested = opt ? opt->sync : RR_SYNC_AUTO;
     const uint32_t flags = opt ? opt->flags : 0;
     if ((flags & RR_FLAG_STREAM_LOADS) && (flags & RR_FLAG_CACHED_LOADS)) return RR_ERR_INVALID;
-    p->block = block;
     p->chunk_len = round_up(ceil_div(count, (uint64_t)R), V);
     p->slice_len = round_up(ceil_div(p->chunk_len, (uint64_t)nslices), V);
     if (phase == 0) {
@@ -1327,9 +1342,6 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     // hop's load: one chunk per rank, N bytes in all
     p->fuse = phase == 0 && R > 1 && (flags & RR_FLAG_FUSED_BOUNDARY) ? 1 : 0;
     p->hbm_bytes = R > 1 ? rs + ag - (p->fuse ? nbytes : 0) : 0;
-
-    const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
-    p->resident_max = resident_limit(d, kernel, block);
 
     // Workgroups per rank (cols): about 16 waves per CU, two 512-thread
     // workgroups.  Each interleaves `depth` lanes and runs `rounds` groups of
@@ -1407,6 +1419,12 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     p->rounds = rounds;
     p->cols = lanes / (depth * rounds);
     p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
+    if (!fixed_block && R >= kLongRingRanks && (uint64_t)R * nbytes > kInfinityCacheBytes &&
+        p->sub_len * elem_bytes(dt) <= kLongRingPieceBytes)
+        block = kLongRingBlock;
+    p->block = block;
+    const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
+    p->resident_max = resident_limit(d, kernel, block);
     // Columns on the XCD map are padded to a multiple of 8 (idle columns exit).
     p->xcd_map = (flags & RR_FLAG_NO_XCD_MAP) ? 0 : 1;
     const uint64_t cols_launched = p->xcd_map ? round_up((uint64_t)p->cols, 8) : p->cols;

@@ -70,7 +70,7 @@ A = 0x7F0000000000  # 16-byte aligned addresses; never dereferenced by these tes
     dict(ptrs=[A + 4096, A, A + 4096 + 16], count=8),           # overlap after sorting
     dict(ptrs=[A, A + 4096], count=16, sync=9),
     dict(ptrs=[A, A + 4096], count=16, sync="per_peer"),   # barrier runs only
-    dict(ptrs=[A, A + 4096], count=16, block=128),
+    dict(ptrs=[A, A + 4096], count=16, block=192),
     dict(ptrs=[A, A + 4096], count=16, team=-1),
     dict(ptrs=[A, A + 4096], count=16, rounds=-1),
     dict(ptrs=[A, A + 4096], count=16, depth=5),
@@ -186,7 +186,7 @@ def test_product_path_has_no_oracle_dependency():
 
 
 @pytest.mark.parametrize("phase,opts", [
-    (0, dict(team=4097)), (0, dict(rounds=5000)), (0, dict(depth=5)), (0, dict(block=128)),
+    (0, dict(team=4097)), (0, dict(rounds=5000)), (0, dict(depth=5)), (0, dict(block=192)),
     (0, dict(sync=4)), (2, dict(team=-1)), (3, dict(team=4097)), (4, dict(rounds=-1)),
     (5, dict(block=96)), (6, dict(sync=2)), (6, dict(team=65537)),
 ])

@@ -89,6 +89,25 @@ def test_stream_loads_small_ragged(rr, dtype, op, R, count, nslices, team, sync)
         assert_matches_oracle(got, want, dtype, f"R={R} count={count} {opts}")
 
 
+def test_long_ring_block_plan(rr):
+    """Automatic workgroup size: 128 threads for 16 ranks or more over buffers
+    larger than the Infinity Cache when a lane's piece is at most 64 KiB, with
+    the columns a 512-thread plan would have; 512 otherwise; an explicit size
+    is kept."""
+    for sync in ("p2p", "barrier"):
+        p = rr.plan(64, 8 << 20, "fp32", 8, sync=sync)          # 32 MiB per rank
+        assert p["block"] == 128 and p["sub_len"] * 4 <= 64 << 10
+        q = rr.plan(64, 8 << 20, "fp32", 8, sync=sync, block=512)
+        assert (p["grid"], p["team"], p["depth"], p["rounds"]) == \
+            (q["grid"], q["team"], q["depth"], q["rounds"])
+    assert rr.plan(16, 16 << 20, "fp32", 4, sync="barrier")["block"] == 128   # 64 KiB pieces
+    assert rr.plan(16, 16 << 20, "fp32", 4, sync="p2p")["block"] == 512       # 128 KiB pieces
+    assert rr.plan(8, 16 << 20, "fp32", 4)["block"] == 512                    # short ring
+    p = rr.plan(16, 4 << 20, "fp32", 4, sync="barrier")                      # 256 MiB: fits
+    assert p["block"] == 512 and p["sub_len"] * 4 <= 64 << 10
+    assert rr.plan(64, 8 << 20, "fp32", 8, block=256)["block"] == 256
+
+
 def test_stream_loads_plan(rr):
     """Default: non-temporal once the R buffers exceed the 256 MB Infinity Cache."""
     assert rr.plan(8, 16 << 20, "fp32", 4)["stream_loads"] == 1        # 512 MiB
@@ -254,7 +273,7 @@ def test_invariance_across_slices_modes_teams(rr):
     ref = None
     for nslices in (1, 2, 4, 8, 16):
         for sync in ("p2p", "barrier", "launch"):
-            for team, block, depth in ((1, 256, 1), (4, 512, 2), (0, 1024, 0)):
+            for team, block, depth in ((1, 256, 1), (4, 512, 2), (0, 1024, 0), (2, 128, 2)):
                 log(f"case invariance ns={nslices} sync={sync} team={team} block={block}")
                 got = run_case(rr, x, dtype, "sum", nslices, sync=sync, team=team, block=block,
                                depth=depth)
