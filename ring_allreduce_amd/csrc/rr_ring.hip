@@ -47,12 +47,23 @@ constexpr int kSlots = RR_MAX_SLICES * RR_MAX_RANKS;  // (context, rank) pairs
 constexpr uint64_t kDefaultTimeoutNs = 2000000000ull;
 // Bytes one hop of the lanes in flight may move (3 N / rounds over all ranks):
 // fewer keep a partial cached until the next hop reads it, more save hand-offs.
-// Fitted on MI355X over R = 2..64 and 512 MiB..4 GiB in all: max(96 MiB,
-// 12 MiB x R) with predecessor hand-offs, twice that with a barrier per hop,
-// which waits for all R ranks of a lane and so prefers fewer, larger rounds
-// (mean 0.4% and 0.8% slower than the best power-of-two rounds of each case).
+// Predecessor hand-offs: max(96 MiB, 12 MiB x R), one lane per workgroup.  A
+// long ring (16 ranks or more) whose hop moves at least 384 MiB over all ranks
+// interleaves two lanes per workgroup instead, with 384 MiB in flight.  A
+// barrier per hop waits for all R ranks of a lane and prefers fewer, larger
+// rounds: 48 MiB x R, within [192, 384] MiB, two lanes per workgroup.  Fitted on
+// MI355X to two sweeps of R = 2..64 x 32 MiB..1 GiB per rank (56 cases, depth 1
+// and 2, rounds 1..64): 1.5% slower than the best plan of each case on average,
+// against 2.4% for the earlier budget (max(96 MiB, 12 MiB x R), doubled for the
+// barrier; one lane per workgroup without one), which lost 8-13% at 64 ranks x
+// 256 MiB and 5-8% with predecessor hand-offs at 16 ranks x 128 MiB..1 GiB.
 constexpr uint64_t kRoundBytesMin = 96ull << 20;
 constexpr uint64_t kRoundBytesPerRank = 12ull << 20;
+constexpr uint64_t kWideHopBytes = 384ull << 20;
+constexpr uint64_t kWideRoundBytes = 384ull << 20;
+constexpr uint64_t kBarrierRoundPerRank = 48ull << 20;
+constexpr uint64_t kBarrierRoundMin = 192ull << 20;
+constexpr uint64_t kBarrierRoundMax = 384ull << 20;
 // The staged loop bounds one step of the lanes in flight the same way: 192 MiB
 // for its AllReduce and ReduceScatter (a sweep of R = 2..64, 512 MiB..4 GiB:
 // 1.2% and 0.5% from the best power-of-two rounds on average).  Its AllGather
@@ -69,9 +80,11 @@ constexpr uint64_t kInfinityCacheBytes = 256ull << 20;
 // Lanes a workgroup interleaves when the caller does not choose: a per-hop
 // barrier waits for the slowest of R workgroups, which a second lane hides; a
 // predecessor hand-off is cheap enough that a second lane costs more than it
-// hides (measured on MI355X).
+// hides, except on a long ring moving a wide hop (see the rounds budget above;
+// measured on MI355X).
 constexpr int kAutoDepthBarrier = 2;
 constexpr int kAutoDepthP2P = 1;
+constexpr int kAutoDepthWide = 2;
 // Workgroup size when the caller does not choose.  Columns are planned for
 // 512-thread workgroups (two per CU); a long ring (16 ranks or more) over
 // buffers larger than the Infinity Cache whose lane pieces are at most 64 KiB
@@ -1351,16 +1364,20 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     const int target_cols = std::max(1, d->cus * 16 * 64 / block / R);
     const bool fixed_depth = opt && opt->depth > 0;
     const bool fixed_rounds = opt && opt->rounds > 0;
+    const bool barrier = requested == RR_SYNC_BARRIER;
+    const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
+    const bool wide = !barrier && R >= kLongRingRanks && hop_bytes >= kWideHopBytes;
     int depth = fixed_depth ? opt->depth
-                            : (requested == RR_SYNC_BARRIER ? kAutoDepthBarrier : kAutoDepthP2P);
+                            : (barrier ? kAutoDepthBarrier : wide ? kAutoDepthWide : kAutoDepthP2P);
     int rounds;
     if (fixed_rounds) {
         rounds = opt->rounds;
     } else {
-        const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
         const uint64_t per_round =
-            std::max<uint64_t>(kRoundBytesMin, (uint64_t)R * kRoundBytesPerRank) *
-            (requested == RR_SYNC_BARRIER ? 2 : 1);
+            barrier ? std::min(kBarrierRoundMax,
+                               std::max(kBarrierRoundMin, (uint64_t)R * kBarrierRoundPerRank))
+            : wide  ? kWideRoundBytes
+                    : std::max<uint64_t>(kRoundBytesMin, (uint64_t)R * kRoundBytesPerRank);
         uint64_t k = 1;  // a power of two: lanes split evenly over the XCDs
         while (k * per_round < hop_bytes) k *= 2;
         rounds = (int)k;

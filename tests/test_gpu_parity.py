@@ -108,6 +108,27 @@ def test_long_ring_block_plan(rr):
     assert rr.plan(64, 8 << 20, "fp32", 8, block=256)["block"] == 256
 
 
+def test_depth_and_rounds_plan(rr):
+    """Automatic lanes per workgroup and rounds: predecessor hand-offs keep one
+    lane and max(96 MiB, 12 MiB x R) of a hop in flight, except a long ring whose
+    hop moves 384 MiB or more (two lanes, 384 MiB); a barrier per hop keeps two
+    lanes and 48 MiB x R within [192, 384] MiB."""
+    def dk(R, mib, sync, dtype="fp32", ns=4):
+        p = rr.plan(R, mib * (1 << 20) // (4 if dtype == "fp32" else 2), dtype, ns, sync=sync)
+        return p["depth"], p["rounds"]
+    assert dk(8, 64, "p2p") == (1, 2)                       # 192 MiB per hop, 96 per round
+    assert dk(8, 256, "p2p", "bf16", 8) == (1, 8)
+    assert dk(64, 32, "p2p", ns=8) == (1, 1)                # 96 MiB per hop: not wide
+    assert dk(16, 64, "p2p") == (1, 1)                      # 192 MiB per hop, 192 per round
+    assert dk(16, 256, "p2p") == (2, 2)                     # wide: 768 MiB per hop
+    assert dk(16, 1024, "p2p") == (2, 8)
+    assert dk(64, 32, "barrier", ns=8) == (2, 1)
+    assert dk(64, 256, "barrier") == (2, 2)                 # 384 MiB per round
+    assert dk(16, 1024, "barrier") == (2, 8)
+    assert dk(4, 256, "barrier") == (2, 4)                  # 192 MiB per round
+    assert dk(8, 256, "barrier") == (2, 2)
+
+
 def test_stream_loads_plan(rr):
     """Default: non-temporal once the R buffers exceed the 256 MB Infinity Cache."""
     assert rr.plan(8, 16 << 20, "fp32", 4)["stream_loads"] == 1        # 512 MiB
