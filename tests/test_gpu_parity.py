@@ -478,6 +478,15 @@ def test_full_r16_sweep(rr, k):
         _full_size(rr, workloads.r16_sweep(k, op, ns), 4000)
 
 
+def test_full_r16_p2p_two_lanes(rr):
+    """Predecessor hand-offs with two lanes per workgroup (the automatic plan of
+    a long ring with a wide hop): 16 ranks x 256 MiB."""
+    w = workloads.r16_sweep(8, "sum", 4).with_(sync="p2p")
+    p = rr.plan(w.R, w.count, w.dtype, w.nslices, sync="p2p")
+    assert p["depth"] == 2 and p["sync"] == "p2p"
+    _full_size(rr, w, 4000)
+
+
 def test_full_r16_1GiB(rr):
     """The largest point of the R=16 sweep: 1 GiB per rank, 16 GiB in all."""
     _full_size(rr, workloads.r16_sweep(9, "sum", 16), 3000)
