@@ -515,11 +515,11 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
 //                   (r - k) mod R.
 constexpr int kFifoSlots = 2;
 constexpr int kStagedBlock = 512;
-// AlltoAll: one 1024-thread workgroup per CU, 4 vectors per thread in flight
-// (against 256 threads x 8: +3% at 8 ranks x 64 MiB fp32, +9% bf16 256 MiB, +4%
-// at 64 ranks)
+// AlltoAll: one 1024-thread workgroup per CU, 8 vectors per thread in flight
+// (4 in flight: 2-4% slower at 8 ranks x 64 MiB fp32, bf16 256 MiB and 64 ranks
+// x 32 MiB; 256 threads x 8: 3-9% slower)
 constexpr int kA2ABlock = 1024;
-constexpr int kA2AUnroll = 4;
+constexpr int kA2AUnroll = 8;
 constexpr int kCopyBlock = 512;
 constexpr int kCopyPerCU = 4;
 constexpr int kA2AWavesPerCU = 16;
