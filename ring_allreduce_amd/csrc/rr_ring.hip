@@ -520,8 +520,8 @@ constexpr int kStagedBlock = 512;
 // x 32 MiB; 256 threads x 8: 3-9% slower)
 constexpr int kA2ABlock = 1024;
 constexpr int kA2AUnroll = 8;
-constexpr int kCopyBlock = 512;
-constexpr int kCopyPerCU = 4;
+constexpr int kCopyBlock = 1024;
+constexpr int kCopyPerCU = 2;
 constexpr int kA2AWavesPerCU = 16;
 enum : int { MODE_ALLREDUCE = 0, MODE_RS = 1, MODE_AG = 2 };
 enum : int { P_SEND = 0, P_RRS = 1, P_RRCS = 2, P_RCS = 3, P_RECV = 4, P_RRC = 5, P_CS = 6 };
@@ -1074,9 +1074,11 @@ __global__ void __launch_bounds__(256) fill_u64_kernel(uint64_t* p, uint64_t n, 
 
 // Streaming copy: the bandwidth reference for the ring kernels.  Each
 // workgroup copies one contiguous span (DRAM pages stay open longer than with a
-// grid-wide stride); nontemporal hints, as the data are touched once.  512
-// threads x 8 vectors in flight, 4 workgroups per CU: 5.9 TB/s on MI355X, where
-// 256-thread workgroups reach 5.6 at any grid size.
+// grid-wide stride); nontemporal hints, as the data are touched once.  1024
+// threads x 8 vectors in flight, 2 workgroups per CU: 6.06-6.08 TB/s on MI355X,
+// the best of a probe over span layouts, hints, grids of 256-4096, 256-1024
+// threads and 4-16 vectors per thread (512 threads x 8, 4 per CU: 5.82-5.91;
+// 256-thread workgroups: 5.6 at any grid size).
 __global__ void __launch_bounds__(kCopyBlock) copy_kernel(const u32x4* __restrict__ src,
                                                           u32x4* __restrict__ dst, uint64_t nvec,
                                                           const uint8_t* __restrict__ src_tail,
