@@ -154,10 +154,12 @@ typedef enum {
 typedef struct {
     int32_t sync;        /* rr_sync_t */
     int32_t team;        /* workgroups per (rank, slice); 0 = choose */
-    int32_t block;       /* threads per workgroup: 128, 256, 512 or 1024; 0 = automatic:
-                            512, or 128 when R >= 16, the R buffers together exceed
-                            256 MiB and a lane's piece of a chunk is at most 64 KiB
-                            (columns are planned for 512 either way) */
+    int32_t block;       /* threads per workgroup: 128, 256, 512 or 1024; 0 = automatic,
+                            from the lane piece p (the bytes a workgroup moves per
+                            lane and hop): 128 if p <= 2 KiB, 256 if 16 KiB < p <=
+                            32 KiB, 128 if p <= 64 KiB with R >= 16 and the R
+                            buffers together above 256 MiB, else 512 (columns are
+                            planned for 512 either way) */
     int32_t rounds;      /* lane groups each workgroup runs one after another
                             (depth * rounds must divide slices * team);
                             0 = choose from the buffer size */

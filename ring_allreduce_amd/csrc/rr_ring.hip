@@ -86,16 +86,27 @@ constexpr int kAutoDepthBarrier = 2;
 constexpr int kAutoDepthP2P = 1;
 constexpr int kAutoDepthWide = 2;
 // Workgroup size when the caller does not choose.  Columns are planned for
-// 512-thread workgroups (two per CU); a long ring (16 ranks or more) over
-// buffers larger than the Infinity Cache whose lane pieces are at most 64 KiB
-// then runs them with 128 threads.  A workgroup's hop ends when its slowest
-// wave's stores have drained, and along a long chain of hand-offs those tails
-// add up; a shorter ring streams better with 512 threads.  Measured on MI355X,
-// same columns: 16-64 ranks x 8-64 MiB, 2-15% faster with 128 threads; 4-8
-// ranks, pieces of 128 KiB and more, or buffers that fit the cache (16 ranks x
-// 16 MiB: 6% slower in barrier mode), even or slower.
+// 512-thread workgroups (two per CU); the threads per workgroup then follow the
+// lane piece (the bytes one workgroup moves per lane and hop):
+//   at most 2 KiB (a latency-bound call)                          128 threads
+//   16-32 KiB                                                      256
+//   at most 64 KiB on a long ring (16 ranks or more) over buffers
+//   larger than the Infinity Cache                                 128
+//   otherwise                                                      512
+// A workgroup's hop ends when its slowest wave's stores have drained, and along
+// a long chain of hand-offs those tails add up, so fewer waves per workgroup pay
+// when a piece is small; a piece of 64 KiB or more on a shorter ring streams
+// better with 512.  Fitted on MI355X to 90 cases at fixed columns (R = 4..64,
+// 4 KiB..256 MiB per rank, both modes, 128 / 256 / 512 threads): 0.6% slower than
+// the best size of each case on average (worst 9%, pieces of 4-16 KiB, where no
+// size wins consistently), against 4.2% (worst 31%) for 512 everywhere but the
+// long-ring rule.
 constexpr int kAutoBlock = 512;
-constexpr int kLongRingBlock = 128;
+constexpr int kSmallBlock = 128;
+constexpr int kMidBlock = 256;
+constexpr uint64_t kTinyPieceBytes = 2ull << 10;
+constexpr uint64_t kMidPieceLo = 16ull << 10;   // exclusive
+constexpr uint64_t kMidPieceHi = 32ull << 10;
 constexpr int kLongRingRanks = 16;
 constexpr uint64_t kLongRingPieceBytes = 64ull << 10;
 
@@ -1438,9 +1449,16 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     p->rounds = rounds;
     p->cols = lanes / (depth * rounds);
     p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
-    if (!fixed_block && R >= kLongRingRanks && (uint64_t)R * nbytes > kInfinityCacheBytes &&
-        p->sub_len * elem_bytes(dt) <= kLongRingPieceBytes)
-        block = kLongRingBlock;
+    if (!fixed_block) {
+        const uint64_t piece = p->sub_len * elem_bytes(dt);
+        if (piece <= kTinyPieceBytes)
+            block = kSmallBlock;
+        else if (piece > kMidPieceLo && piece <= kMidPieceHi)
+            block = kMidBlock;
+        else if (R >= kLongRingRanks && (uint64_t)R * nbytes > kInfinityCacheBytes &&
+                 piece <= kLongRingPieceBytes)
+            block = kSmallBlock;
+    }
     p->block = block;
     const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
     p->resident_max = resident_limit(d, kernel, block);

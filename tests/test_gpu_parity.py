@@ -89,23 +89,27 @@ def test_stream_loads_small_ragged(rr, dtype, op, R, count, nslices, team, sync)
         assert_matches_oracle(got, want, dtype, f"R={R} count={count} {opts}")
 
 
-def test_long_ring_block_plan(rr):
-    """Automatic workgroup size: 128 threads for 16 ranks or more over buffers
-    larger than the Infinity Cache when a lane's piece is at most 64 KiB, with
-    the columns a 512-thread plan would have; 512 otherwise; an explicit size
-    is kept."""
+def test_automatic_block_plan(rr):
+    """Automatic workgroup size from the lane piece p, with the columns a
+    512-thread plan would have: 128 if p <= 2 KiB, 256 if 16 KiB < p <= 32 KiB,
+    128 if p <= 64 KiB on a long ring over buffers beyond the Infinity Cache,
+    else 512; an explicit size is kept."""
+    def pb(R, count, ns, sync, **kw):
+        p = rr.plan(R, count, "fp32", ns, sync=sync, **kw)
+        return p["block"], p["sub_len"] * 4, p
     for sync in ("p2p", "barrier"):
-        p = rr.plan(64, 8 << 20, "fp32", 8, sync=sync)          # 32 MiB per rank
-        assert p["block"] == 128 and p["sub_len"] * 4 <= 64 << 10
+        b, piece, p = pb(64, 8 << 20, 8, sync)                  # 32 MiB per rank
+        assert (b, piece) == ((128, 65536) if sync == "p2p" else (256, 32768))
         q = rr.plan(64, 8 << 20, "fp32", 8, sync=sync, block=512)
         assert (p["grid"], p["team"], p["depth"], p["rounds"]) == \
             (q["grid"], q["team"], q["depth"], q["rounds"])
-    assert rr.plan(16, 16 << 20, "fp32", 4, sync="barrier")["block"] == 128   # 64 KiB pieces
-    assert rr.plan(16, 16 << 20, "fp32", 4, sync="p2p")["block"] == 512       # 128 KiB pieces
-    assert rr.plan(8, 16 << 20, "fp32", 4)["block"] == 512                    # short ring
-    p = rr.plan(16, 4 << 20, "fp32", 4, sync="barrier")                      # 256 MiB: fits
-    assert p["block"] == 512 and p["sub_len"] * 4 <= 64 << 10
-    assert rr.plan(64, 8 << 20, "fp32", 8, block=256)["block"] == 256
+    assert pb(16, 16 << 20, 4, "barrier")[:2] == (128, 65536)   # long ring, 1 GiB in all
+    assert pb(16, 16 << 20, 4, "p2p")[:2] == (512, 131072)
+    assert pb(8, 16 << 20, 4, "p2p")[:2] == (512, 65536)        # short ring
+    assert pb(16, 4 << 20, 4, "barrier")[:2] == (256, 32768)    # 256 MiB in all
+    assert pb(16, 1 << 10, 4, "p2p")[0] == 128                  # 4 KiB per rank
+    assert pb(16, 1 << 18, 4, "p2p")[:2] == (512, 16384)        # 16 KiB: stays 512
+    assert pb(64, 8 << 20, 8, "barrier", block=512)[0] == 512
 
 
 def test_depth_and_rounds_plan(rr):
