@@ -64,6 +64,15 @@
  * workspace (signals, shadows, the error record), allocated on the first call
  * on a device (or by rr_init) and freed by rr_finalize.  The first call on a
  * device must therefore not happen under stream capture.
+ *
+ * GRAPHS.  After that first call, calls may be captured into a HIP graph and
+ * replayed: a call records kernel launches only (no memset or copy nodes), and
+ * everything a kernel must tell apart from one launch to the next (signal
+ * counts, shadows, the per-launch tag of its XCD placement check) lives in the
+ * device workspace and advances on the device, so a replay behaves as a fresh
+ * call.  The staged loop's receive buffers must already be large enough (a
+ * call of the same or larger size made outside capture), since growing them
+ * allocates.
  */
 #ifndef RR_H
 #define RR_H

@@ -110,6 +110,16 @@ constexpr uint64_t kMidPieceHi = 32ull << 10;
 constexpr int kLongRingRanks = 16;
 constexpr uint64_t kLongRingPieceBytes = 64ull << 10;
 
+// Per-launch tag of the XCD table, kept on the device so that a launch replayed
+// from a captured graph still gets a fresh one: every workgroup reads `gen` at
+// start, and the last workgroup to leave a launch advances it for the next
+// launch (launches on one device are ordered, so no launch starts before the
+// previous one has left).  Zero is never used: the table starts zeroed.
+struct LaunchTag {
+    uint64_t* gen;    // current tag, in [1, 2^32)
+    uint64_t* exits;  // workgroups of the running launch that have left
+};
+
 struct RingArgs {
     void* bufs[RR_MAX_RANKS];
     uint64_t count;      // elements per rank
@@ -121,7 +131,7 @@ struct RingArgs {
     uint64_t* xcc_table; // per workgroup: (generation << 8) | XCC id, published at start
     ErrorRecord* err;
     uint64_t timeout_ticks;
-    uint32_t generation; // per-launch tag, never 0
+    LaunchTag launch;    // per-launch tag of the XCD table (device side)
     int32_t fuse;        // 1: fused boundary (the last ReduceScatter hop also does the first AllGather hop)
     int32_t R;
     int32_t team;
@@ -138,6 +148,22 @@ struct RingArgs {
 };
 
 __device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t launch_generation(const LaunchTag& t) {
+    return (uint32_t)__hip_atomic_load(t.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every workgroup once, after all of its work (every exit path).
+__device__ __forceinline__ void leave_launch(const LaunchTag& t) {
+    if (threadIdx.x != 0) return;
+    const uint64_t before =
+        __hip_atomic_fetch_add(t.exits, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1 != (uint64_t)gridDim.x) return;
+    uint32_t next = launch_generation(t) + 1;
+    if (next == 0) next = 1;
+    __hip_atomic_store(t.exits, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(t.gen, (uint64_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ int wrap(int a, int m) {
     const int r = a % m;
@@ -364,7 +390,7 @@ __device__ __forceinline__ void hop_body(bool reduce, bool stream, const void* s
 }
 
 template <int DT, int OP, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
+__device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t generation) {
     constexpr int U = 4;
     const int R = a.R;
     const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
@@ -379,7 +405,7 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
     const uint32_t my_xcc = xcc_id() & 0xFu;
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;  // a recorded failure is sticky
-        if (synced) publish_xcc(a.xcc_table, a.generation, my_xcc);
+        if (synced) publish_xcc(a.xcc_table, generation, my_xcc);
     }
     __syncthreads();
     if (s_stop) return;
@@ -465,11 +491,11 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
                 if (g < a.g_last) {
                     if (!decided) {
                         if (threadIdx.x < 64) {
-                            const int v = column_on_one_xcd(a.xcc_table, a.generation, R, col,
+                            const int v = column_on_one_xcd(a.xcc_table, generation, R, col,
                                                             a.xcd_map != 0, my_xcc, a.err,
                                                             a.timeout_ticks);
                             if (threadIdx.x == 0) {
-                                if (v < 0) record_timeout(a.err, lane[p], r, 0, a.generation, 0);
+                                if (v < 0) record_timeout(a.err, lane[p], r, 0, generation, 0);
                                 s_local = v;
                             }
                         }
@@ -501,6 +527,12 @@ __global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
                 if (p < a.depth) a.shadow[lane[p] * R + r] = shadow[p];  // sig == shadow again
         }
     }
+}
+
+template <int DT, int OP, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
+    ring_body<DT, OP, BLOCK>(a, launch_generation(a.launch));
+    leave_launch(a.launch);
 }
 
 // ------------------------------------------------------ the staged loop --
@@ -561,7 +593,7 @@ struct StagedArgs {
     uint64_t* xcc_table;
     ErrorRecord* err;
     uint64_t timeout_ticks;
-    uint32_t generation;
+    LaunchTag launch;
     uint32_t inject;
     int32_t R;
     int32_t team;
@@ -663,7 +695,7 @@ __device__ __forceinline__ void staged_move(const char* in, const char* local, c
 }
 
 template <int DT, int OP, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
+__device__ __forceinline__ void staged_body(const StagedArgs& a, const uint32_t generation) {
     constexpr int ES = ElemBytes<DT>::value;
     const int R = a.R;
     const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
@@ -679,7 +711,7 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
     const uint32_t my_xcc = xcc_id() & 0xFu;
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;  // a recorded failure is sticky
-        if (synced) publish_xcc(a.xcc_table, a.generation, my_xcc);
+        if (synced) publish_xcc(a.xcc_table, generation, my_xcc);
     }
     __syncthreads();
     if (s_stop) return;
@@ -768,10 +800,10 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
         if (synced) {
             if (!decided) {
                 if (threadIdx.x < 64) {
-                    const int v = column_on_one_xcd(a.xcc_table, a.generation, R, lane,
+                    const int v = column_on_one_xcd(a.xcc_table, generation, R, lane,
                                                     a.xcd_map != 0, my_xcc, a.err, a.timeout_ticks);
                     if (threadIdx.x == 0) {
-                        if (v < 0) record_timeout(a.err, lane, r, 0, a.generation, 0);
+                        if (v < 0) record_timeout(a.err, lane, r, 0, generation, 0);
                         s_local = v;
                     }
                 }
@@ -798,6 +830,12 @@ __global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
         a.credit_shadow[my_slot] = credit_base + (uint64_t)K;
     }
     }  // rounds
+}
+
+template <int DT, int OP, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
+    staged_body<DT, OP, BLOCK>(a, launch_generation(a.launch));
+    leave_launch(a.launch);
 }
 
 // ---------------------------------------------------------------- AlltoAll
@@ -904,7 +942,7 @@ struct BarrierArgs {
     int32_t nsteps;
     int32_t mode;        // SYNC_P2P, SYNC_BARRIER or SYNC_PER_PEER
     int32_t nctx;        // contexts taking part (columns; the grid is padded to 8)
-    uint32_t generation;
+    LaunchTag launch;
     uint32_t inject;
     int32_t audit;       // counting mode: also keep per-peer witnesses and count early passes
     int32_t pad;
@@ -964,7 +1002,7 @@ __device__ PeerWait peer_wait(const uint64_t* slot, bool active, uint64_t target
 //   PER_PEER  one add to this waiter's slot in each other waiter's row; the
 //             waiter expects every slot of its row to advance (the per-peer
 //             layout the pull request replaced)
-__global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
+__device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_t generation) {
     const Place pl = place_of(blockIdx.x, a.R, true);
     const int r = pl.rank, ctx = pl.col;
     if (ctx >= a.nctx || a.nsteps <= 0) return;
@@ -975,14 +1013,14 @@ __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;
         shadow = a.shadow[slot];
-        publish_xcc(a.xcc_table, a.generation, my_xcc);
+        publish_xcc(a.xcc_table, generation, my_xcc);
     }
     __syncthreads();
     if (s_stop) return;
-    const int v = column_on_one_xcd(a.xcc_table, a.generation, a.R, ctx, true, my_xcc, a.err,
+    const int v = column_on_one_xcd(a.xcc_table, generation, a.R, ctx, true, my_xcc, a.err,
                                     a.timeout_ticks);
     if (v < 0) {
-        if (threadIdx.x == 0) record_timeout(a.err, ctx, r, 0, a.generation, 0);
+        if (threadIdx.x == 0) record_timeout(a.err, ctx, r, 0, generation, 0);
         return;
     }
     const bool local = v == 1;
@@ -1075,6 +1113,11 @@ __global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
     if (use_pp && peer_lane) *in_pp_shadow = pp_shadow;
 }
 
+__global__ void __launch_bounds__(64) barrier_kernel(const BarrierArgs a) {
+    barrier_body(a, launch_generation(a.launch));
+    leave_launch(a.launch);
+}
+
 // ------------------------------------------------------ support kernels --
 
 __global__ void __launch_bounds__(256) fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t value,
@@ -1127,7 +1170,8 @@ struct DeviceState {
     uint64_t* credit_shadow = nullptr;
     char* fifo = nullptr;               // staged loop: receive buffers, grown on demand
     size_t fifo_bytes = 0;
-    uint32_t generation = 0;
+    uint64_t* launch_gen = nullptr;     // per-launch tag of the XCD table (starts at 1)
+    uint64_t* launch_exits = nullptr;   // workgroups of the running launch that have left
 };
 
 std::mutex g_mu;
@@ -1172,9 +1216,10 @@ static rr_status_t ensure_device(DeviceState** out) {
             d.wall_khz <= 0)
             d.wall_khz = 100000;  // the gfx9 constant-rate clock runs at 100 MHz
         // signals (one per cache line), shadows, the XCC table, the error record,
-        // then the staged loop's credit signals and their shadows
+        // the staged loop's credit signals and their shadows, then the launch tag
+        // and the exit count (a cache line each)
         const size_t words = 2 * ((size_t)kSlots * kSignalStride + (size_t)kSlots) +
-                             (size_t)kSlots + 16;
+                             (size_t)kSlots + 16 + 2 * kSignalStride;
         void* p = nullptr;
         if (!hip_ok(hipMalloc(&p, words * sizeof(uint64_t)))) return RR_ERR_NOMEM;
         if (!hip_ok(hipMemset(p, 0, words * sizeof(uint64_t)))) {
@@ -1188,6 +1233,14 @@ static rr_status_t ensure_device(DeviceState** out) {
         d.err = (ErrorRecord*)(d.xcc_table + kSlots);
         d.credit = d.xcc_table + kSlots + 16;
         d.credit_shadow = d.credit + (size_t)kSlots * kSignalStride;
+        d.launch_gen = d.credit_shadow + kSlots;
+        d.launch_exits = d.launch_gen + kSignalStride;
+        const uint64_t first_tag = 1;
+        if (!hip_ok(hipMemcpy(d.launch_gen, &first_tag, sizeof first_tag,
+                              hipMemcpyHostToDevice))) {
+            (void)hipFree(p);
+            return RR_ERR_HIP;
+        }
         d.ready = true;
     }
     *out = &d;
@@ -1510,11 +1563,7 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.xcc_table = d->xcc_table;
     a.err = d->err;
     a.timeout_ticks = timeout_ticks(d, opt);
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        if (++d->generation == 0) d->generation = 1;
-        a.generation = d->generation;
-    }
+    a.launch = {d->launch_gen, d->launch_exits};
     a.R = R;
     a.team = p.team;
     a.cols = p.cols;
@@ -1722,11 +1771,7 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
     a.xcc_table = d->xcc_table;
     a.err = d->err;
     a.timeout_ticks = timeout_ticks(d, opt);
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        if (++d->generation == 0) d->generation = 1;
-        a.generation = d->generation;
-    }
+    a.launch = {d->launch_gen, d->launch_exits};
     a.inject = opt ? opt->inject : 0;
     a.R = R;
     a.team = p.team;
@@ -2080,11 +2125,7 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
     a.xcc_table = d->xcc_table;
     a.err = d->err;
     a.nctx = ncontexts;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        if (++d->generation == 0) d->generation = 1;
-        a.generation = d->generation;
-    }
+    a.launch = {d->launch_gen, d->launch_exits};
     a.timeout_ticks = timeout_ticks(d, opt);
     a.expected = expected_per_step;
     a.R = R;
