@@ -2,7 +2,9 @@
 
 Default workload: R=8 virtual ranks, fp32, 64 MiB per rank, SUM, 4 slices.  One
 step is one in-place AllReduce call (2(R-1) ring hops) over all R rank buffers,
-inputs resident in HBM.
+inputs resident in HBM.  The rank buffers are separate tensors, as a caller's
+are (--layout slab carves them from one allocation instead, 256 bytes apart:
+R=64 in barrier mode runs about 4% slower there).
 
 value = algorithmic HBM bytes per call / time per call, with the algorithmic
 bytes of the in-place ring: each ReduceScatter hop reads the incoming and local
@@ -60,6 +62,9 @@ def parse():
                          "alltoall: the per-rank buffer as R blocks, one per receiver")
     ap.add_argument("--fused", action="store_true",
                     help="fuse the last ReduceScatter hop with the first AllGather hop")
+    ap.add_argument("--layout", default="separate", choices=("separate", "slab"),
+                    help="rank buffers as separate tensors (default) or carved from one "
+                         "allocation 256 bytes apart")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -69,6 +74,34 @@ def parse():
                     help="instead of the AllReduce: per-step latency of the counting barrier "
                          "alone for R = 2..64 and 1 or 8 contexts (one JSON line per point)")
     return ap.parse_args()
+
+
+def rank_buffers(rr, torch, R, count, dtype, layout):
+    """The R rank buffers and a snapshot function (call it once, after filling the
+    buffers; it returns a function that copies the inputs back).
+
+    separate: one tensor per rank, as a caller's buffers normally are (torch's
+              caching allocator puts large tensors 2 MiB apart);
+    slab:     R buffers carved from one allocation 256 bytes apart (the layout
+              the parity tests use, with guard bands to catch stray stores)."""
+    if layout == "slab":
+        slabs = rr.make_slabs(R, count, dtype, device="cuda")
+        ranks = slabs.ranks
+
+        def snapshot():
+            saved = slabs.storage.clone()
+            return lambda: slabs.storage.copy_(saved)
+    else:
+        ranks = [torch.empty(count, dtype=dtype, device="cuda") for _ in range(R)]
+
+        def snapshot():
+            saved = [t.clone() for t in ranks]
+
+            def restore():
+                for t, v in zip(ranks, saved):
+                    t.copy_(v)
+            return restore
+    return ranks, snapshot
 
 
 def pick_workload(name):
@@ -125,7 +158,7 @@ def main():
     if args.barrier_latency:
         return barrier_latency(rr, torch)
     if args.r16_sweep:
-        return r16_sweep(rr, torch, np)
+        return r16_sweep(rr, torch, np, args.layout)
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
@@ -158,30 +191,30 @@ def main():
                 "fp16": torch.float16}[w.dtype]
     raw_t = torch.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else torch.int32
     raw_np = np.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else np.int32
-    slabs = rr.make_slabs(w.R, w.count, torch_dt, device="cuda")
+    ranks, restore = rank_buffers(rr, torch, w.R, w.count, torch_dt, args.layout)
     for r in range(w.R):
-        slabs.ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
-    pristine = slabs.storage.clone()
+        ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
+    restore = restore()  # snapshot the inputs; calling it copies them back
     stream = torch.cuda.current_stream()
     kernel = {"ring": "ring_kernel", "alltoall": "alltoall_kernel"}.get(path, "staged_kernel")
 
     if path == "ring":
-        out_bufs = slabs.ranks
+        out_bufs = ranks
 
         def step():
-            rr.allreduce_ring(slabs.ranks, w.op, w.nslices, **opts)
+            rr.allreduce_ring(ranks, w.op, w.nslices, **opts)
     elif path == "staged":
-        out_bufs = rr.make_slabs(w.R, w.count, torch_dt, device="cuda").ranks
+        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
 
         def step():
-            rr.allreduce_ring_staged(slabs.ranks, out_bufs, w.op, w.nslices, **opts)
+            rr.allreduce_ring_staged(ranks, out_bufs, w.op, w.nslices, **opts)
     elif path == "reduce_scatter":
         out_bufs = [torch.empty(blk, dtype=torch_dt, device="cuda") for _ in range(w.R)]
 
         def step():
-            rr.reduce_scatter(slabs.ranks, out_bufs, w.op, w.nslices, **opts)
+            rr.reduce_scatter(ranks, out_bufs, w.op, w.nslices, **opts)
     elif path == "all_gather":
-        ag_send = [t[:blk] for t in slabs.ranks]
+        ag_send = [t[:blk] for t in ranks]
         out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
 
         def step():
@@ -190,7 +223,7 @@ def main():
         out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
 
         def step():
-            rr.alltoall(slabs.ranks, out_bufs)
+            rr.alltoall(ranks, out_bufs)
 
     # one checked call on the pristine inputs, kept for the CPU cross-check
     step()
@@ -200,7 +233,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    slabs.storage.copy_(pristine)
+    restore()
     torch.cuda.synchronize()
     rr.check_kernel_error()
 
@@ -332,7 +365,8 @@ def main():
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
                    "rounds": p["rounds"], "depth": p["depth"], "stream_loads": p["stream_loads"],
                    "fused_boundary": bool(p["fused"]) if path == "ring" else False,
-                   "algorithmic_bytes_per_step": B, "parallelism": "virtual ranks on 1 GPU"},
+                   "algorithmic_bytes_per_step": B, "layout": args.layout,
+                   "parallelism": "virtual ranks on 1 GPU"},
         "timing": timing,
         # ring traffic in the sources' sense: bytes sent over all links per call
         "bus_bytes_per_step": (2 * (w.R - 1) * w.bytes_per_rank if path in ("ring", "staged")
@@ -400,7 +434,7 @@ def barrier_latency(rr, torch):
     return 0
 
 
-def r16_sweep(rr, torch, np):
+def r16_sweep(rr, torch, np, layout="separate"):
     """The R=16 fp32 sweep, 4 KiB * 4^k per rank (k = 0..9): SUM with 1, 4 and 16
     slices and MAX with 4, each in barrier and p2p mode.  Per point: inputs
     restored, 2 warm-up calls, then 10 calls timed with HIP events on the launch
@@ -411,22 +445,22 @@ def r16_sweep(rr, torch, np):
     for k in range(10):
         w0 = workloads.r16_sweep(k, "sum", 4)
         x = workloads.inputs(w0)
-        slabs = rr.make_slabs(w0.R, w0.count, torch.float32, device="cuda")
+        ranks, restore = rank_buffers(rr, torch, w0.R, w0.count, torch.float32, layout)
         for r in range(w0.R):
-            slabs.ranks[r].copy_(torch.from_numpy(x[r]))
+            ranks[r].copy_(torch.from_numpy(x[r]))
         del x
-        pristine = slabs.storage.clone()
+        restore = restore()
         for op, ns in (("sum", 1), ("sum", 4), ("sum", 16), ("max", 4)):
             for sync in ("barrier", "p2p"):
                 p = rr.plan(w0.R, w0.count, "fp32", ns, sync=sync)
-                slabs.storage.copy_(pristine)
+                restore()
                 for _ in range(2):
-                    rr.allreduce_ring(slabs.ranks, op, ns, sync=sync)
+                    rr.allreduce_ring(ranks, op, ns, sync=sync)
                 a = torch.cuda.Event(enable_timing=True)
                 e = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 for _ in range(10):
-                    rr.allreduce_ring(slabs.ranks, op, ns, sync=sync)
+                    rr.allreduce_ring(ranks, op, ns, sync=sync)
                 e.record(stream)
                 torch.cuda.synchronize()
                 rr.check_kernel_error()
@@ -437,10 +471,10 @@ def r16_sweep(rr, torch, np):
                                   "GB/s": round(B / ms / 1e6, 1),
                                   "pct_of_peak": round(100 * B / ms / 1e6 / HBM_PEAK_GBS, 2),
                                   "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],
-                                  "block": p["block"], "grid": p["grid"],
+                                  "block": p["block"], "grid": p["grid"], "layout": layout,
                                   "stream_loads": p["stream_loads"], "launches": p["launches"]}),
                       flush=True)
-        del slabs, pristine
+        del ranks, restore
         torch.cuda.empty_cache()
     return 0
 
