@@ -1,5 +1,6 @@
-"""GPU parity of the in-place ring for fp16 and for MIN and PROD: the HIP kernels
-against the CPU oracle, element by element, bit for bit."""
+"""GPU parity of the in-place ring for fp16, for MIN and PROD, and for special
+values in every type: the HIP kernels against the CPU oracle, element by element,
+bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -90,3 +91,56 @@ def test_ops_with_rounds_depth_and_fusion(rr):
         log(f"case fp16 {opts}")
         got = _run(rr, x, "fp16", "sum", ns, **opts)
         assert_matches_oracle(got, want, "fp16", f"fp16 {opts}")
+
+
+def _special_pairs(dtype, rng):
+    """Bit patterns that exercise the fold's edge cases, plus random bits (NaN and
+    infinity patterns included) for the floating types."""
+    if dtype == "fp32":
+        inf, ninf, qnan, snan = 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001
+        maxf, minsub, maxsub, one, mone = 0x7F7FFFFF, 0x00000001, 0x007FFFFF, 0x3F800000, 0xBF800000
+        pairs = [(inf, one), (ninf, one), (inf, ninf), (qnan, one), (one, snan), (0xFFC12345, one),
+                 (maxf, maxf), (maxf, 0x73800000), (minsub, minsub), (maxsub, minsub),
+                 (0x80000000, 0x80000000), (0x80000000, 0), (one, mone), (0x00800000, 0x80000001),
+                 (0x33800000, one), (0x33800001, one), (0x4B800000, 0x3F000000), (minsub, 0x3F000000)]
+        extra = rng.integers(0, 1 << 32, size=(4000, 2), dtype=np.uint64)
+        raw = np.uint32
+    elif dtype == "bf16":
+        inf, ninf, qnan = 0x7F80, 0xFF80, 0x7FC0
+        pairs = [(inf, 0x3F80), (ninf, 0x3F80), (inf, ninf), (qnan, 0x3F80), (0x3F80, 0x7F81),
+                 (0x7F7F, 0x7F7F), (0x7F7F, 0x7B00), (0x0001, 0x0001), (0x007F, 0x0001),
+                 (0x8000, 0x8000), (0x8000, 0x0000), (0x3F80, 0xBF80), (0x3F80, 0x3B80),
+                 (0x3F81, 0x3B80), (0x4380, 0x3F00), (0x0001, 0x3F00), (0x1000, 0x1000)]
+        extra = rng.integers(0, 1 << 16, size=(4000, 2), dtype=np.uint64)
+        raw = np.uint16
+    else:
+        imax, imin = 0x7FFFFFFF, 0x80000000
+        pairs = [(imax, 1), (imin, 0xFFFFFFFF), (imax, imax), (imin, imin), (imax, imin),
+                 (0x10000, 0x10000), (0xFFFFFFFF, 0xFFFFFFFF), (0, imin), (46341, 46341)]
+        extra = rng.integers(0, 1 << 32, size=(4000, 2), dtype=np.uint64)
+        raw = np.uint32
+    allp = pairs + [(int(a), int(b)) for a, b in extra]
+    a = np.array([p[0] for p in allp], dtype=np.uint64).astype(raw)
+    b = np.array([p[1] for p in allp], dtype=np.uint64).astype(raw)
+    view = {"fp32": np.float32, "bf16": np.uint16, "int32": np.int32}[dtype]
+    return a.view(view), b.view(view), raw
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "int32"])
+@pytest.mark.parametrize("R", [2, 3])
+def test_specials_through_the_ring(rr, dtype, R):
+    """Special values through the ring's folds, bit for bit against the oracle:
+    infinities, NaN (fp32 compared as "both NaN", bf16 canonical 0x7FC0),
+    overflow to infinity, subnormal operands and results (kept, not flushed),
+    signed zeros, rounding ties, and int32 wrap-around in SUM and PROD.  With
+    R = 3 the chunk values pass through two folds."""
+    rng = np.random.default_rng(11 + R)
+    a, b, raw = _special_pairs(dtype, rng)
+    x = [a.copy(), b.copy()]
+    if R == 3:
+        x.append(rng.permutation(b).copy())
+    for op in ("sum", "prod", "max", "min"):
+        log(f"case specials {dtype} R={R} {op}")
+        got = _run(rr, [t.copy() for t in x], dtype, op, 1)
+        assert_matches_oracle(got, oracle_expect([t.copy() for t in x], op), dtype,
+                              f"specials {dtype} R={R} {op}")
