@@ -156,7 +156,7 @@ def main():
         return 1
     torch.cuda.set_device(0)
     if args.barrier_latency:
-        return barrier_latency(rr, torch)
+        return barrier_latency(rr, torch, np)
     if args.r16_sweep:
         return r16_sweep(rr, torch, np, args.layout)
     w = pick_workload(args.workload)
@@ -377,7 +377,7 @@ def main():
     return 0
 
 
-def barrier_latency(rr, torch):
+def barrier_latency(rr, torch, np):
     """Per-step latency of the barrier on its own, in three layouts: one 64-lane
     workgroup per (context, waiter); per step each waiter arrives and waits.
       barrier   counting signal: adds 1 to each other waiter's one signal, waits
@@ -385,7 +385,10 @@ def barrier_latency(rr, torch):
       per_peer  per-peer slots: adds 1 to its own slot in each other waiter's
                 row, waits for each of the R-1 slots of its row to advance by 1
       p2p       adds 1 to its successor's signal, waits for 1
-    us/step = (t(nsteps) - t(0)) / nsteps, best of 5 timed launches each.  Then,
+    us/step = (t(nsteps) - t(0)) / nsteps, best of 5 timed launches each; beside it
+    the in-kernel distribution of step times (the device clock stamped when each
+    waiter's wait for each step is over) and the spread between the first and
+    the last waiter of a context leaving the same step.  Then,
     for the counting barrier, audited runs count the steps a waiter passed on a
     stand-in arrival from a peer one step ahead (a lower bound)."""
     rr.init()
@@ -415,11 +418,28 @@ def barrier_latency(rr, torch):
                 t1 = timed(R, steps, nctx, mode)
                 us = (t1 - t0) * 1e3 / steps
                 per_waiter = 1 if mode == "p2p" else R - 1
+                # in-kernel view: each waiter's step times from the device clock, and
+                # how far apart the waiters of a context leave the same step
+                st, khz = b.run_timed(R, steps, nctx, mode=mode)
+                torch.cuda.synchronize()
+                rr.check_kernel_error()
+                stamps = st.cpu().numpy()
+                to_us = 1e3 / khz
+                step_us = np.diff(stamps[:, :, 1:], axis=2).ravel() * to_us
+                spread_us = (stamps[:, :, 1:].max(axis=1) - stamps[:, :, 1:].min(axis=1)).ravel() * to_us
+                pct = lambda a, q: round(float(np.percentile(a, q)), 3)
                 print(json.dumps({"metric": "barrier latency per step", "mode": mode,
                                   "R": R, "contexts": nctx, "us_per_step": round(us, 3),
                                   "atomics_per_step": nctx * R * per_waiter,
                                   "slots_per_waiter": 1 if mode != "per_peer" else R - 1,
-                                  "empty_launch_ms": round(t0, 4)}), flush=True)
+                                  "empty_launch_ms": round(t0, 4),
+                                  "in_kernel_step_us": {"p50": pct(step_us, 50),
+                                                        "p90": pct(step_us, 90),
+                                                        "p99": pct(step_us, 99),
+                                                        "max": round(float(step_us.max()), 3)},
+                                  "exit_spread_us": {"p50": pct(spread_us, 50),
+                                                     "max": round(float(spread_us.max()), 3)},
+                                  "clock_khz": khz}), flush=True)
     for R in (4, 8, 16, 64):
         nctx, asteps = 8, 500
         b.reset()

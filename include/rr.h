@@ -383,6 +383,24 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t *b, int R, int nsteps, in
                                  uint64_t expected_per_step, const rr_options_t *opt,
                                  rr_stream_t stream);
 
+/* counting_barrier_run, with the in-kernel step times that the per-step latency
+   is read from (the latency measurement the DeepEP pull request's "Performance"
+   section makes for the network barrier, here taken on the device).  `stamps`
+   is caller-owned device memory of ncontexts * R * (nsteps + 1) uint64 words,
+   8-byte aligned; for context c and waiter q, word (c * R + q) * (nsteps + 1)
+   receives the device's constant-rate wall clock before that waiter's first
+   step, and word ... + k the clock when its wait for step k was over (k =
+   1..nsteps).  *clock_khz receives that clock's rate (host pointer).  One clock
+   serves the whole device, so stamps of different waiters compare directly.
+   Stamps of a waiter whose wait failed stay as they were.  The call allocates
+   nothing.  Errors: as counting_barrier_run, plus RR_ERR_INVALID for a null or
+   misaligned `stamps`, a null `clock_khz` or, unless RR_FLAG_NO_POINTER_CHECK,
+   a `stamps` range outside one device allocation. */
+rr_status_t counting_barrier_run_timed(rr_counting_barrier_t *b, int R, int nsteps,
+                                       int ncontexts, uint64_t expected_per_step,
+                                       const rr_options_t *opt, uint64_t *stamps,
+                                       uint32_t *clock_khz, rr_stream_t stream);
+
 /* ---------------------------------------------------------------- support */
 
 /* Waits for `stream`, then reports and clears the device's failure record.

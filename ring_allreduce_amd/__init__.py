@@ -123,6 +123,8 @@ _cb_read_peer = _sig("counting_barrier_read_peer", _i, _vp, _i, _i, _i, ctypes.P
                      ctypes.POINTER(_u64))
 _cb_early = _sig("counting_barrier_early_passes", _i, _vp, _i, _i, ctypes.POINTER(_u64))
 _cb_run = _sig("counting_barrier_run", _i, _vp, _i, _i, _i, _u64, _OPT, _vp)
+_cb_run_timed = _sig("counting_barrier_run_timed", _i, _vp, _i, _i, _i, _u64, _OPT, _vp,
+                     ctypes.POINTER(ctypes.c_uint32), _vp)
 _last_kernel_error = _sig("rr_last_kernel_error", _i, _vp, ctypes.POINTER(ErrorRecord))
 _init = _sig("rr_init", _i)
 _workspace_preset = _sig("rr_workspace_preset", _i, _u64, _vp)
@@ -137,7 +139,7 @@ EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allredu
             "reduce_scatter", "all_gather", "alltoall", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
             "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
-            "counting_barrier_early_passes", "counting_barrier_run",
+            "counting_barrier_early_passes", "counting_barrier_run", "counting_barrier_run_timed",
             "rr_last_kernel_error", "rr_init", "rr_workspace_preset", "rr_hbm_copy",
             "rr_status_string", "rr_abi_version", "rr_finalize"]
 
@@ -428,6 +430,23 @@ class CountingBarrier:
         o = _options(sync=mode, **opts)
         _check(_cb_run(self._h, R, nsteps, ncontexts, expected, ctypes.byref(o),
                        _stream_handle(stream)), "counting_barrier_run")
+
+    def run_timed(self, R: int, nsteps: int, ncontexts: int = 1, expected: int | None = None,
+                  mode: str = "barrier", stream=None, **opts):
+        """``run`` with in-kernel timestamps.  Returns (stamps, clock_khz): stamps
+        is a uint64 tensor on the GPU of shape (ncontexts, R, nsteps + 1), the
+        device's constant-rate clock before each waiter's first step and when each
+        of its steps' waits was over (valid once the stream has synchronised)."""
+        if expected is None:
+            expected = R - 1 if mode == "barrier" else 1
+        dev = torch.device("cuda", torch.cuda.current_device())
+        stamps = torch.zeros((ncontexts, R, nsteps + 1), dtype=torch.int64, device=dev)
+        khz = ctypes.c_uint32()
+        o = _options(sync=mode, **opts)
+        _check(_cb_run_timed(self._h, R, nsteps, ncontexts, expected, ctypes.byref(o),
+                             stamps.data_ptr(), ctypes.byref(khz), _stream_handle(stream)),
+               "counting_barrier_run_timed")
+        return stamps, khz.value
 
     def read(self, ctx: int, waiter: int):
         v, s = _u64(), _u64()

@@ -943,6 +943,7 @@ struct BarrierArgs {
     int32_t mode;        // SYNC_P2P, SYNC_BARRIER or SYNC_PER_PEER
     int32_t nctx;        // contexts taking part (columns; the grid is padded to 8)
     LaunchTag launch;
+    uint64_t* stamps;    // optional: wall clock per (context, waiter): start, then each step
     uint32_t inject;
     int32_t audit;       // counting mode: also keep per-peer witnesses and count early passes
     int32_t pad;
@@ -1042,6 +1043,11 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
     // until the end).  Its step-2 arrival must be held too: otherwise it stands
     // in for its own late step-1 arrival, which both layouts allow.
     const bool defer = (a.inject & RR_INJECT_DEFER_ARRIVAL) && injected && peer_lane && q == 1;
+    // optional timestamps: the constant-rate wall clock before the first step and
+    // when each step's wait is over (lane 0 of the waiter's wave)
+    uint64_t* const stamps =
+        a.stamps ? a.stamps + (uint64_t)(ctx * a.R + r) * (uint64_t)(a.nsteps + 1) : nullptr;
+    if (stamps && lane == 0) stamps[0] = wall_clock64();
 
     auto arrive = [&]() {
         if (per_peer) {
@@ -1077,6 +1083,7 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
             pp_shadow = target;
             if (lane == 0) acquire_stores(local);
             __syncthreads();
+            if (stamps && lane == 0) stamps[step] = wall_clock64();
         } else {
             if (lane == 0) {
                 uint64_t target = shadow + a.expected;
@@ -1091,6 +1098,7 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
             }
             __syncthreads();
             if (s_stop) return;
+            if (stamps && lane == 0) stamps[step] = wall_clock64();
             if (audit) {
                 bool missing = false;
                 if (peer_lane) {
@@ -2103,9 +2111,9 @@ rr_status_t counting_barrier_early_passes(rr_counting_barrier_t* b, int ctx, int
                : RR_ERR_HIP;
 }
 
-rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, int ncontexts,
-                                 uint64_t expected_per_step, const rr_options_t* opt,
-                                 rr_stream_t stream) {
+static rr_status_t run_barrier(rr_counting_barrier_t* b, int R, int nsteps, int ncontexts,
+                               uint64_t expected_per_step, const rr_options_t* opt,
+                               uint64_t* stamps, rr_stream_t stream) {
     if (!b || R < 1 || R > b->nwaiters || ncontexts < 1 || ncontexts > b->ncontexts || nsteps < 0)
         return RR_ERR_INVALID;
     if (opt && (opt->sync < RR_SYNC_AUTO || opt->sync > RR_SYNC_PER_PEER)) return RR_ERR_INVALID;
@@ -2136,6 +2144,7 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
                   : opt->sync == RR_SYNC_PER_PEER ? SYNC_PER_PEER : SYNC_BARRIER;
     a.inject = opt ? opt->inject : 0;
     a.audit = opt && (opt->flags & RR_FLAG_AUDIT) ? 1 : 0;
+    a.stamps = stamps;
     void* args[] = {&a};
     hipStream_t s = (hipStream_t)stream;
     const bool coop = opt && (opt->flags & RR_FLAG_COOPERATIVE);
@@ -2149,6 +2158,32 @@ rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, in
         hipLaunchKernelGGL(barrier_kernel, dim3(grid), dim3(64), 0, s, a);
     }
     return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
+}
+
+rr_status_t counting_barrier_run(rr_counting_barrier_t* b, int R, int nsteps, int ncontexts,
+                                 uint64_t expected_per_step, const rr_options_t* opt,
+                                 rr_stream_t stream) {
+    return run_barrier(b, R, nsteps, ncontexts, expected_per_step, opt, nullptr, stream);
+}
+
+rr_status_t counting_barrier_run_timed(rr_counting_barrier_t* b, int R, int nsteps,
+                                       int ncontexts, uint64_t expected_per_step,
+                                       const rr_options_t* opt, uint64_t* stamps,
+                                       uint32_t* clock_khz, rr_stream_t stream) {
+    if (!b || !stamps || !clock_khz || R < 1 || R > b->nwaiters || ncontexts < 1 ||
+        ncontexts > b->ncontexts || nsteps < 0 || (uintptr_t)stamps % 8 != 0)
+        return RR_ERR_INVALID;
+    if (!(opt && (opt->flags & RR_FLAG_NO_POINTER_CHECK))) {
+        void* const buf[1] = {stamps};
+        const size_t bytes = (size_t)ncontexts * R * ((size_t)nsteps + 1) * sizeof(uint64_t);
+        rr_status_t st = check_extents(buf, 1, bytes);
+        if (st != RR_OK) return st;
+    }
+    DeviceState* d = nullptr;
+    rr_status_t st = ensure_device(&d);
+    if (st != RR_OK) return st;
+    *clock_khz = (uint32_t)d->wall_khz;
+    return run_barrier(b, R, nsteps, ncontexts, expected_per_step, opt, stamps, stream);
 }
 
 rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {

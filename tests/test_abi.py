@@ -214,3 +214,15 @@ def test_build_script_loads_without_the_library():
             "assert callable(m.build) and m.LIB.endswith('librr.so'); "
             "assert 'ring_allreduce_amd' not in sys.modules")
     subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, check=True)
+
+
+def test_timed_barrier_run_validates_on_host(rr):
+    """counting_barrier_run_timed rejects a missing object, stamps buffer or
+    clock out-pointer before any device work."""
+    khz = ctypes.c_uint32()
+    assert rr._cb_run_timed(None, 2, 1, 1, 1, None, A, ctypes.byref(khz), None) == \
+        rr.RR_ERR_INVALID
+    fake = ctypes.c_void_p(A)
+    assert rr._cb_run_timed(fake, 2, 1, 1, 1, None, None, ctypes.byref(khz), None) == \
+        rr.RR_ERR_INVALID
+    assert rr._cb_run_timed(fake, 2, 1, 1, 1, None, A, None, None) == rr.RR_ERR_INVALID

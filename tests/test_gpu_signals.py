@@ -276,3 +276,39 @@ def test_plan_of_the_benchmark_workload(rr):
     assert p["sync"] == "launch" and p["launches"] == 126
     with pytest.raises(rr.RRError):
         rr.plan(64, 1 << 24, "fp32", 1024, sync="p2p")
+
+
+@pytest.mark.parametrize("mode", ["barrier", "per_peer", "p2p"])
+@pytest.mark.parametrize("R,nctx", [(2, 1), (5, 3), (16, 2), (64, 8)])
+def test_step_stamps_show_the_ordering(rr, mode, R, nctx):
+    """In-kernel step times (one device-wide constant-rate clock): every waiter's
+    stamps are non-decreasing, and no waiter leaves step k before the peers it
+    waits for have left step k-1 (all other waiters of its context for the
+    counting and per-peer barriers, the predecessor for p2p).  The stamp of step
+    k-1 is taken before the peer's step-k arrival, which the waiter must see
+    before taking its own stamp of step k, so the order is strict in time."""
+    log(f"case stamps mode={mode} R={R} nctx={nctx}")
+    b = rr.CountingBarrier(64, 8)
+    nsteps = 200
+    st, khz = b.run_timed(R, nsteps, nctx, mode=mode)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert khz > 0
+    s = st.cpu().numpy()
+    assert s.shape == (nctx, R, nsteps + 1)
+    assert (s > 0).all()
+    assert (np.diff(s, axis=2) >= 0).all()
+    before, after = s[:, :, :-1], s[:, :, 1:]      # step k-1 and step k, k = 1..nsteps
+    if mode == "p2p":
+        pred = np.roll(before, 1, axis=1)            # waiter q's predecessor q-1
+        assert (after >= pred).all()
+    else:
+        for q in range(R):
+            others = np.delete(before, q, axis=1).max(axis=1)
+            assert (after[:, q] >= others).all(), f"waiter {q} left a step early"
+    # the untimed run counts the same as the timed one
+    for c in range(nctx):
+        for q in range(R):
+            v, sh = b.read(c, q)
+            assert v == sh
+    b.close()
