@@ -1,0 +1,304 @@
+// rr_ring_kernel.hip -- the in-place ring kernel (ReduceScatter, AllGather and
+// the AllReduce that chains them) over virtual ranks on one MI355X.
+//
+// Method (post "Why AllReduce = ReduceScatter + AllGather -- with NCCL Ring
+// AllReduce", loosp.cn, sections 4-6): global hop g = 1 .. 2(R-1).  Hops 1..R-1
+// are the ReduceScatter rounds: rank r folds chunk (r - g + 1) mod R of its own
+// buffer (the partial it received last round, or its input in round 1) into the
+// same chunk of its successor's buffer.  Hops R..2R-2 are the AllGather rounds
+// t = g - (R-1): rank r copies chunk (r + 2 - t) mod R into its successor's
+// buffer.  Rank r's hop g needs only rank r-1's hop g-1 (its data), and every
+// earlier reader of what it overwrites is an ancestor of that chain, so a
+// predecessor hand-off per hop is all the ordering the ring needs.
+//
+// Work decomposition: chunk -> `nslices` slices -> `team` sub-ranges.  A lane is
+// one (slice j, member w) pair; workgroup (r, lane) owns that sub-range for rank
+// r in every chunk, so its hop-g input was written by workgroup (r-1, lane) at
+// hop g-1.  Every lane is an independent context with one 64-bit signal per
+// rank: after each hop the producer adds 1 to its successor's signal and the
+// consumer advances its shadow by 1 and waits (P2P); or, for a per-hop barrier,
+// every workgroup of the lane adds 1 to all R-1 other ranks' signals and each
+// waiter advances its shadow by R-1 (the counting barrier of the DeepEP pull
+// request "make the rail barrier a counting barrier", section "Fix").
+//
+// One producer per rank per signal is what makes the count safe to hand data
+// over.  Had the W workgroups of a slice shared one signal, a workgroup running
+// a hop ahead could supply the increment of a teammate that has not finished --
+// the hazard the same pull request describes for anonymous counting (section
+// "Scoped to the rail team": a count says that enough arrived, not who) -- and
+// the consumer of that teammate's sub-range would read stale data.
+#include "rr_kernels.hpp"
+
+namespace rr {
+
+// One hop of one workgroup over elements [lo, hi) of both buffers.  ReduceScatter:
+// dst = fold(src, dst).  AllGather: dst = src, bit for bit.  16-byte vectors,
+// U vectors per thread in flight, then a scalar tail (only at the ragged end).
+template <int DT, int OP, int BLOCK, int U, int AUX>
+__device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void* dstbuf,
+                                          void* dst2buf, uint64_t lo, uint64_t hi) {
+    constexpr int ES = ElemBytes<DT>::value;
+    constexpr int V = 16 / ES;
+    const uint64_t n = hi - lo;
+    const uint32_t nv = (uint32_t)(n / V);
+    const char* sb = (const char*)srcbuf + lo * ES;
+    const __amdgpu_buffer_rsrc_t rs = incoming(sb, n * ES);
+    u32x4* __restrict__ d = (u32x4*)((char*)dstbuf + lo * ES);
+    u32x4* d2 = dst2buf ? (u32x4*)((char*)dst2buf + lo * ES) : nullptr;
+    uint32_t i = threadIdx.x;
+    if (reduce && d2) {
+        // recvReduceCopySend: the finished chunk goes to the owner's buffer and on
+        // to the owner's successor in the same pass
+        for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
+            u32x4 x[U], y[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+#pragma unroll
+            for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 v = fold4<DT, OP>(x[u], y[u]);
+                d[i + u * BLOCK] = v;
+                d2[i + u * BLOCK] = v;
+            }
+        }
+        for (; i < nv; i += BLOCK) {
+            const u32x4 v = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
+            d[i] = v;
+            d2[i] = v;
+        }
+    } else if (reduce) {
+        for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
+            u32x4 x[U], y[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+#pragma unroll
+            for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
+#pragma unroll
+            for (int u = 0; u < U; ++u) d[i + u * BLOCK] = fold4<DT, OP>(x[u], y[u]);
+        }
+        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
+    } else {
+        constexpr int UC = 2 * U;
+        for (; i + (UC - 1) * BLOCK < nv; i += UC * BLOCK) {
+            u32x4 x[UC];
+#pragma unroll
+            for (int u = 0; u < UC; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+#pragma unroll
+            for (int u = 0; u < UC; ++u) d[i + u * BLOCK] = x[u];
+        }
+        for (; i < nv; i += BLOCK) d[i] = load_in<AUX>(rs, i);
+    }
+    const uint64_t t = (uint64_t)nv * V + threadIdx.x;  // fewer than V elements remain
+    if (t < n) {
+        char* dp = (char*)dstbuf + (lo + t) * ES;
+        const int off = (int)(t * ES);
+        char* dp2 = dst2buf ? (char*)dst2buf + (lo + t) * ES : nullptr;
+        if constexpr (ES == 2) {
+            const uint16_t in =
+                __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, AUX);
+            const uint16_t v =
+                reduce ? (uint16_t)Fold<DT, OP>::half(in, *(const uint16_t*)dp) : in;
+            *(uint16_t*)dp = v;
+            if (dp2) *(uint16_t*)dp2 = v;
+        } else {
+            const uint32_t in = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, AUX);
+            const uint32_t v = reduce ? Fold<DT, OP>::lane(in, *(const uint32_t*)dp) : in;
+            *(uint32_t*)dp = v;
+            if (dp2) *(uint32_t*)dp2 = v;
+        }
+    }
+}
+
+template <int DT, int OP, int BLOCK, int U>
+__device__ __forceinline__ void hop_body(bool reduce, bool stream, const void* srcbuf,
+                                         void* dstbuf, void* dst2buf, uint64_t lo, uint64_t hi) {
+    constexpr uint64_t kPiece = kPieceBytes / ElemBytes<DT>::value;  // elements, vector multiple
+    for (uint64_t p = lo; p < hi; p += kPiece) {
+        const uint64_t q = umin(p + kPiece, hi);
+        if (stream)
+            hop_piece<DT, OP, BLOCK, U, kAuxRingIncoming>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+        else
+            hop_piece<DT, OP, BLOCK, U, kAuxDeviceScope>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+    }
+}
+
+template <int DT, int OP, int BLOCK>
+__device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t generation) {
+    constexpr int U = 4;
+    const int R = a.R;
+    const Place pl = place_of(blockIdx.x, R, a.xcd_map != 0);
+    const int r = pl.rank, col = pl.col;
+    if (col >= a.cols) return;  // padding column
+    const int succ = r + 1 == R ? 0 : r + 1;
+    const int succ2 = succ + 1 == R ? 0 : succ + 1;
+    const bool synced = a.g_last > a.g_first;
+
+    __shared__ int s_stop;
+    __shared__ int s_local;
+    const uint32_t my_xcc = xcc_id() & 0xFu;
+    if (threadIdx.x == 0) {
+        s_stop = sig_read(&a.err->flag) != 0;  // a recorded failure is sticky
+        if (synced) publish_xcc(a.xcc_table, generation, my_xcc);
+    }
+    __syncthreads();
+    if (s_stop) return;
+    // Producer side of the hand-off (release_stores), fixed at the first
+    // hand-off of the launch: `local` when all R workgroups of the column run on
+    // one XCD and so share its L2.  The consumer side (acquire_stores) is the
+    // same either way; its L1 invalidation matters even within one XCD, because a
+    // workgroup re-reads a chunk of its incoming buffer (the partial in
+    // ReduceScatter, the finished chunk one AllGather hop later).
+    bool local = false;
+    bool decided = false;
+    const uint64_t arrivals = a.sync == SYNC_BARRIER ? (uint64_t)(R - 1) : 1;
+    __shared__ int s_stop_lane[kMaxDepth];
+
+    // Lane groups one after another: only cols * depth lanes are in flight at
+    // once, so the partial a hop writes is still cached when the next hop reads
+    // it, whatever the buffer size.  Within a group the workgroup interleaves its
+    // `depth` lanes hop by hop -- hop g of lane 1 runs while lane 0's hand-off
+    // for hop g+1 completes.  Every wait targets a (lane, hop) that comes earlier
+    // in the (hop, lane) order all workgroups follow, so the interleave cannot
+    // deadlock.
+    for (int round = 0; round < a.rounds; ++round) {
+        int lane[kMaxDepth];
+        uint64_t off_lo[kMaxDepth], off_hi[kMaxDepth], shadow[kMaxDepth];
+#pragma unroll
+        for (int p = 0; p < kMaxDepth; ++p) {
+            lane[p] = col + (round * a.depth + p) * a.cols;
+            const int j = lane[p] / a.team;
+            const int w = lane[p] - j * a.team;
+            off_lo[p] = (uint64_t)j * a.slice_len + (uint64_t)w * a.sub_len;
+            off_hi[p] = umin(off_lo[p] + a.sub_len,
+                             umin((uint64_t)(j + 1) * a.slice_len, a.chunk_len));
+            shadow[p] = 0;
+            if (p < a.depth && synced && threadIdx.x == 0) shadow[p] = a.shadow[lane[p] * R + r];
+        }
+
+        for (int g = a.g_first; g <= a.g_last; ++g) {
+#pragma unroll
+            for (int p = 0; p < kMaxDepth; ++p) {
+                if (p >= a.depth) break;
+                const int my_slot = lane[p] * R + r;
+                const bool injected = r == 0 && lane[p] == 0;
+                if (g > a.g_first) {
+                    if (threadIdx.x == 0) {
+                        uint64_t target = shadow[p] + arrivals;
+                        if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected &&
+                            g == a.g_first + 1)
+                            target += 1;
+                        const WaitResult res = sig_wait(&a.sig[(uint64_t)my_slot * kSignalStride],
+                                                        target, a.err, a.timeout_ticks,
+                                                        a.long_nap != 0);
+                        if (res.status == WAIT_TIMEOUT)
+                            record_timeout(a.err, lane[p], r, g, target, res.observed);
+                        shadow[p] = target;
+                        s_stop_lane[p] = res.status != WAIT_OK;
+                        acquire_stores(local);
+                    }
+                    __syncthreads();
+                    if (s_stop_lane[p]) return;
+                }
+
+                int c;
+                bool reduce;
+                if (g <= R - 1) {
+                    c = wrap(r - g + 1, R);
+                    reduce = true;
+                } else {
+                    c = wrap(r + 2 - (g - (R - 1)), R);
+                    reduce = false;
+                }
+                // Fused boundary: the last ReduceScatter hop also stores the finished
+                // chunk in the owner's successor, so the first AllGather hop only
+                // passes the hand-off on.
+                void* dst2 = a.fuse && g == R - 1 ? a.bufs[succ2] : nullptr;
+                const bool skip = a.fuse && g == R;
+                const uint64_t base = (uint64_t)c * a.chunk_len;
+                const uint64_t lo = base + off_lo[p];
+                const uint64_t hi = umin(base + off_hi[p], a.count);
+                if (lo < hi && !skip)
+                    hop_body<DT, OP, BLOCK, U>(reduce, a.stream_in != 0, a.bufs[r], a.bufs[succ],
+                                               dst2, lo, hi);
+
+                if (g < a.g_last) {
+                    if (!decided) {
+                        if (threadIdx.x < 64) {
+                            const int v = column_on_one_xcd(a.xcc_table, generation, R, col,
+                                                            a.xcd_map != 0, my_xcc, a.err,
+                                                            a.timeout_ticks);
+                            if (threadIdx.x == 0) {
+                                if (v < 0) record_timeout(a.err, lane[p], r, 0, generation, 0);
+                                s_local = v;
+                            }
+                        }
+                        __syncthreads();
+                        if (s_local < 0) return;
+                        local = s_local == 1;
+                        decided = true;
+                    }
+                    release_stores(local);
+                    __syncthreads();
+                    const bool drop =
+                        (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && g == a.g_first;
+                    if (!drop) {
+                        if (a.sync == SYNC_BARRIER) {
+                            if ((int)threadIdx.x < R - 1) {
+                                const int q = wrap(r + 1 + (int)threadIdx.x, R);
+                                sig_add(&a.sig[(uint64_t)(lane[p] * R + q) * kSignalStride], 1);
+                            }
+                        } else if (threadIdx.x == 0) {
+                            sig_add(&a.sig[(uint64_t)(lane[p] * R + succ) * kSignalStride], 1);
+                        }
+                    }
+                }
+            }
+        }
+        if (synced && threadIdx.x == 0) {
+#pragma unroll
+            for (int p = 0; p < kMaxDepth; ++p)
+                if (p < a.depth) a.shadow[lane[p] * R + r] = shadow[p];  // sig == shadow again
+        }
+    }
+}
+
+template <int DT, int OP, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
+    ring_body<DT, OP, BLOCK>(a, launch_generation(a.launch));
+    leave_launch(a.launch);
+}
+
+template <int DT, int OP>
+static RingKernel ring_kernel_for_block(int block) {
+    switch (block) {
+        case 128: return ring_kernel<DT, OP, 128>;
+        case 256: return ring_kernel<DT, OP, 256>;
+        case 512: return ring_kernel<DT, OP, 512>;
+        case 1024: return ring_kernel<DT, OP, 1024>;
+        default: return nullptr;
+    }
+}
+
+template <int DT>
+static RingKernel ring_kernel_for_op(int op, int block) {
+    switch (op) {
+        case RR_SUM: return ring_kernel_for_block<DT, OP_SUM>(block);
+        case RR_MAX: return ring_kernel_for_block<DT, OP_MAX>(block);
+        case RR_MIN: return ring_kernel_for_block<DT, OP_MIN>(block);
+        case RR_PROD: return ring_kernel_for_block<DT, OP_PROD>(block);
+        default: return nullptr;
+    }
+}
+
+RingKernel pick_ring_kernel(int dt, int op, int block) {
+    switch (dt) {
+        case RR_INT32: return ring_kernel_for_op<DT_I32>(op, block);
+        case RR_FP32: return ring_kernel_for_op<DT_F32>(op, block);
+        case RR_BF16: return ring_kernel_for_op<DT_BF16>(op, block);
+        case RR_FP16: return ring_kernel_for_op<DT_F16>(op, block);
+        default: return nullptr;
+    }
+}
+
+}  // namespace rr

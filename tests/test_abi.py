@@ -34,6 +34,15 @@ def test_header_declares_the_boundary():
         assert required in names
 
 
+def test_library_exports_nothing_but_the_header(rr):
+    """The dynamic interface is exactly what include/rr.h declares: kernel handles and
+    internal helpers of the library stay local."""
+    out = subprocess.run(["nm", "-D", "--defined-only", rr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines())
+    assert exported == _declared_functions()
+
+
 def test_library_exports_every_declared_symbol(rr):
     names = _declared_functions()
     out = subprocess.run(["nm", "-D", "--defined-only", rr.LIB_PATH], capture_output=True,
