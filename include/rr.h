@@ -168,7 +168,10 @@ typedef struct {
                             lane and hop): 128 if p <= 2 KiB, 256 if 16 KiB < p <=
                             32 KiB, 128 if p <= 64 KiB with R >= 16 and the R
                             buffers together above 256 MiB, else 512 (columns are
-                            planned for 512 either way) */
+                            planned for 512 either way); except RR_SYNC_BARRIER
+                            with R >= 16, 8 R dividing the CU count and 3 x the
+                            per-rank bytes >= 1.5 GiB: 1024, columns planned for
+                            one workgroup per CU */
     int32_t rounds;      /* lane groups each workgroup runs one after another
                             (depth * rounds must divide slices * team);
                             0 = choose from the buffer size */

@@ -70,7 +70,8 @@ constexpr int kAutoDepthWide = 2;
 // 4 KiB..256 MiB per rank, both modes, 128 / 256 / 512 threads): 0.6% slower than
 // the best size of each case on average (worst 9%, pieces of 4-16 KiB, where no
 // size wins consistently), against 4.2% (worst 31%) for 512 everywhere but the
-// long-ring rule.
+// long-ring rule.  One exception plans its columns for 1024 threads: a barrier
+// per hop on a long ring with a wide hop (below).
 constexpr int kAutoBlock = 512;
 constexpr int kSmallBlock = 128;
 constexpr int kMidBlock = 256;
@@ -79,6 +80,16 @@ constexpr uint64_t kMidPieceLo = 16ull << 10;   // exclusive
 constexpr uint64_t kMidPieceHi = 32ull << 10;
 constexpr int kLongRingRanks = 16;
 constexpr uint64_t kLongRingPieceBytes = 64ull << 10;
+// A barrier per hop on a long ring whose hop moves at least 1.5 GiB over all
+// ranks (512 MiB per rank and more) runs one 1024-thread workgroup per CU
+// instead of two of 512, still two lanes per workgroup and the same bytes per
+// round: fewer, larger pieces per barrier.  Measured on MI355X with interleaved
+// repeats: +6.0% and +3.2% at 16 ranks x 512 MiB and 1 GiB, +1.0% and +3.1% at
+// 32 ranks; within +-1% at 256 MiB per rank and with predecessor hand-offs, and
+// worse at 8 ranks, so only this case takes it.  It needs whole columns of 8
+// (8 R dividing the CU count: 16 and 32 ranks on 256 CUs).
+constexpr uint64_t kWideBarrierHopBytes = 1536ull << 20;
+constexpr int kWideBarrierBlock = 1024;
 
 // ------------------------------------------------------------- host side --
 
@@ -269,6 +280,11 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     const bool fixed_block = opt && opt->block;
     int block = fixed_block ? opt->block : kAutoBlock;
     const int requested = opt ? opt->sync : RR_SYNC_AUTO;
+    const bool barrier = requested == RR_SYNC_BARRIER;
+    const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
+    const bool wide_barrier = !fixed_block && barrier && R >= kLongRingRanks &&
+                              hop_bytes >= kWideBarrierHopBytes && d->cus % (8 * R) == 0;
+    if (wide_barrier) block = kWideBarrierBlock;
     const uint32_t flags = opt ? opt->flags : 0;
     if ((flags & RR_FLAG_STREAM_LOADS) && (flags & RR_FLAG_CACHED_LOADS)) return RR_ERR_INVALID;
     p->chunk_len = round_up(ceil_div(count, (uint64_t)R), V);
@@ -292,15 +308,13 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     p->hbm_bytes = R > 1 ? rs + ag - (p->fuse ? nbytes : 0) : 0;
 
     // Workgroups per rank (cols): about 16 waves per CU, two 512-thread
-    // workgroups.  Each interleaves `depth` lanes and runs `rounds` groups of
+    // workgroups (one of 1024 for a wide barrier hop).  Each interleaves `depth` lanes and runs `rounds` groups of
     // them one after another; rounds bound one hop of the lanes in flight
     // (3 N / rounds bytes over all ranks), so that a partial is still cached
     // when the next hop reads it.
     const int target_cols = std::max(1, d->cus * 16 * 64 / block / R);
     const bool fixed_depth = opt && opt->depth > 0;
     const bool fixed_rounds = opt && opt->rounds > 0;
-    const bool barrier = requested == RR_SYNC_BARRIER;
-    const uint64_t hop_bytes = 3ull * (uint64_t)count * elem_bytes(dt);
     const bool wide = !barrier && R >= kLongRingRanks && hop_bytes >= kWideHopBytes;
     int depth = fixed_depth ? opt->depth
                             : (barrier ? kAutoDepthBarrier : wide ? kAutoDepthWide : kAutoDepthP2P);
@@ -371,7 +385,7 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     p->rounds = rounds;
     p->cols = lanes / (depth * rounds);
     p->sub_len = round_up(ceil_div(p->slice_len, (uint64_t)team), V);
-    if (!fixed_block) {
+    if (!fixed_block && !wide_barrier) {
         const uint64_t piece = p->sub_len * elem_bytes(dt);
         if (piece <= kTinyPieceBytes)
             block = kSmallBlock;

@@ -112,6 +112,27 @@ def test_automatic_block_plan(rr):
     assert pb(64, 8 << 20, 8, "barrier", block=512)[0] == 512
 
 
+def test_wide_barrier_block_plan(rr):
+    """A barrier per hop on a long ring moving at least 1.5 GiB per hop (512 MiB per
+    rank and more) runs one 1024-thread workgroup per CU, two lanes each, with the
+    rounds of the 512-thread plan; predecessor hand-offs, shorter rings, smaller
+    buffers and an explicit size keep the other rules."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for R, mib in ((16, 512), (16, 1024), (32, 512)):
+        count = mib * (1 << 20) // 4
+        p = rr.plan(R, count, "fp32", 4, sync="barrier")
+        if cus % (8 * R):
+            continue
+        q = rr.plan(R, count, "fp32", 4, sync="p2p")
+        assert (p["block"], p["grid"], p["depth"]) == (1024, cus, 2), p
+        assert p["rounds"] == q["rounds"]
+        assert q["block"] == 512
+    assert rr.plan(16, 64 << 20, "fp32", 4, sync="barrier", block=512)["block"] == 512
+    assert rr.plan(16, 32 << 20, "fp32", 4, sync="barrier")["block"] == 512    # 128 MiB
+    assert rr.plan(16, 64 << 20, "bf16", 4, sync="barrier")["block"] == 512    # 128 MiB
+    assert rr.plan(8, 256 << 20, "fp32", 4, sync="barrier")["block"] == 512    # short ring
+
+
 def test_depth_and_rounds_plan(rr):
     """Automatic lanes per workgroup and rounds: predecessor hand-offs keep one
     lane and max(96 MiB, 12 MiB x R) of a hop in flight, except a long ring whose
@@ -494,6 +515,29 @@ def test_full_r16_p2p_two_lanes(rr):
 def test_full_r16_1GiB(rr):
     """The largest point of the R=16 sweep: 1 GiB per rank, 16 GiB in all."""
     _full_size(rr, workloads.r16_sweep(9, "sum", 16), 3000)
+
+
+def test_full_r16_1GiB_barrier(rr):
+    """The same point with a barrier per hop: the wide-hop plan (one 1024-thread
+    workgroup per CU, two lanes each)."""
+    w = workloads.r16_sweep(9, "max", 4).with_(sync="barrier")
+    p = rr.plan(w.R, w.count, w.dtype, w.nslices, sync="barrier")
+    log(f"case full r16 1GiB barrier plan={p}")
+    _full_size(rr, w, 3000)
+
+
+def test_wide_barrier_plan_mid_size(rr):
+    """The wide barrier plan's shape (1024 threads, one workgroup per CU, two lanes,
+    several rounds) forced on 32 ranks x 4 MiB + a ragged tail, against the oracle."""
+    R, count, ns, cols = 32, (1 << 20) + 4 * 32 * 7 + 3, 4, 8
+    for op, dtype in (("sum", "fp32"), ("max", "bf16")):
+        x = workloads.generate(R, count, dtype, DIST[dtype], 501)
+        opts = dict(sync="barrier", block=1024, team=cols * 2 * 2 // ns, depth=2, rounds=2)
+        p = rr.plan(R, count, dtype, ns, **opts)
+        assert (p["block"], p["depth"], p["rounds"]) == (1024, 2, 2), p
+        log(f"case wide barrier shape R={R} {dtype} {op} plan={p}")
+        got = run_case(rr, x, dtype, op, ns, **opts)
+        assert_matches_oracle(got, oracle_expect(x, op), dtype, f"wide barrier {dtype} {op}")
 
 
 def test_pieces_longer_than_one_descriptor(rr):
