@@ -1,0 +1,116 @@
+"""Seeded random plans of the in-place ring against the CPU oracle.
+
+Each case draws ranks, a ragged size, element type, reduction, slices, hand-off
+mode, workgroup size, team, lanes per workgroup, rounds, boundary fusion, and
+whether the AllReduce runs as one call or as ReduceScatter then AllGather.  A
+combination the planner accepts must give the oracle's bits on every rank and
+leave the guard words around every rank buffer intact; a combination it rejects
+must be rejected by the call too, before anything is launched (an empty buffer
+is a no-op whatever the plan)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_util import (assert_matches_oracle, guards_intact, log, oracle_expect, to_host,
+                            to_slabs)
+
+pytestmark = pytest.mark.gpu
+
+CASES = 96
+RANKS = [2, 3, 4, 5, 7, 8, 12, 16, 24, 32, 48, 64]
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_allreduce_amd
+    ring_allreduce_amd.init()
+    return ring_allreduce_amd
+
+
+def _dist(dtype, op):
+    if op == "prod":
+        return "unit_jitter"
+    return {"int32": "int_pm1000", "fp32": "uniform_pm1", "bf16": "normal", "fp16": "normal"}[dtype]
+
+
+def _draw(k):
+    g = np.random.default_rng(90_000 + k)
+    R = int(g.choice(RANKS))
+    if g.random() < 0.25:                       # a few vectors per rank, or fewer than R
+        count = int(g.integers(0, 16 * R + 1))
+    else:
+        count = int(g.integers(1, 120_000))
+    case = dict(
+        R=R, count=count,
+        dtype=str(g.choice(["int32", "fp32", "bf16", "fp16"])),
+        op=str(g.choice(["sum", "max", "min", "prod"])),
+        ns=int(g.integers(1, 17)),
+        sync=str(g.choice(["auto", "p2p", "barrier", "launch"])),
+        block=int(g.choice([0, 128, 256, 512, 1024])),
+        team=int(g.choice([0, 0, 1, 2, 3, 5, 8])),
+        depth=int(g.choice([0, 0, 1, 2, 3, 4])),
+        rounds=int(g.choice([0, 0, 1, 2, 3, 4])),
+        split=bool(g.random() < 0.2),
+    )
+    case["fused"] = bool(not case["split"] and g.random() < 0.25)
+    return case
+
+
+def _opts(c):
+    o = dict(sync=c["sync"], block=c["block"], team=c["team"], depth=c["depth"],
+             rounds=c["rounds"])
+    if c["fused"]:
+        o["fused"] = True
+    return o
+
+
+def _accepted(rr, c, phase):
+    try:
+        rr.plan(c["R"], c["count"], c["dtype"], c["ns"], phase=phase, **_opts(c))
+        return True
+    except rr.RRError:
+        return False
+
+
+@pytest.mark.parametrize("k", range(CASES))
+def test_random_plan_matches_oracle(rr, k):
+    c = _draw(k)
+    phases = ("reduce_scatter", "all_gather") if c["split"] else ("allreduce",)
+    ok = [_accepted(rr, c, ph) for ph in phases]
+    log(f"case fuzz {k}: {c} accepted={ok}")
+    x = workloads.generate(c["R"], c["count"], c["dtype"], _dist(c["dtype"], c["op"]), 500 + k)
+    slabs = to_slabs(rr, x, c["dtype"])
+    before = [to_host(t, c["dtype"]) for t in slabs.ranks]
+    calls = {
+        "allreduce": lambda: rr.allreduce_ring(slabs.ranks, c["op"], c["ns"], **_opts(c)),
+        "reduce_scatter": lambda: rr.reduce_scatter_ring(slabs.ranks, c["op"], c["ns"], **_opts(c)),
+        "all_gather": lambda: rr.all_gather_ring(slabs.ranks, c["ns"], **_opts(c)),
+    }
+    if c["count"] == 0:                           # a no-op whatever the plan
+        for ph in phases:
+            calls[ph]()
+        torch.cuda.synchronize()
+        rr.check_kernel_error()
+        assert guards_intact(slabs, c["dtype"], 0)
+        return
+    if not all(ok):
+        # the first phase the planner rejects must fail as a call, launching nothing
+        first = phases[ok.index(False)]
+        if first == "all_gather":
+            pytest.skip("the gather half alone is rejected; the scatter half is covered elsewhere")
+        with pytest.raises(rr.RRError):
+            calls[first]()
+        torch.cuda.synchronize()
+        for r in range(c["R"]):
+            assert np.array_equal(to_host(slabs.ranks[r], c["dtype"]), before[r])
+        return
+    for ph in phases:
+        calls[ph]()
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(slabs, c["dtype"], c["count"]), "a kernel wrote outside the rank buffers"
+    got = [to_host(t, c["dtype"]) for t in slabs.ranks]
+    assert_matches_oracle(got, oracle_expect(x, c["op"]), c["dtype"], f"fuzz case {k}")
