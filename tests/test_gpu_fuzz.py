@@ -17,7 +17,7 @@ from tests.gpu_util import (assert_matches_oracle, guards_intact, log, oracle_ex
 
 pytestmark = pytest.mark.gpu
 
-CASES = 96
+CASES = 192
 RANKS = [2, 3, 4, 5, 7, 8, 12, 16, 24, 32, 48, 64]
 
 
