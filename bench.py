@@ -455,8 +455,8 @@ def barrier_latency(rr, torch, np):
 
 
 def r16_sweep(rr, torch, np, layout="separate"):
-    """The R=16 fp32 sweep, 4 KiB * 4^k per rank (k = 0..9): SUM with 1, 4 and 16
-    slices and MAX with 4, each in barrier and p2p mode.  Per point: inputs
+    """The R=16 fp32 sweep, 4 KiB * 4^k per rank (k = 0..9): SUM with 1, 2, 4, 8 and
+    16 slices and MAX with 4, each in barrier and p2p mode.  Per point: inputs
     restored, 2 warm-up calls, then 10 calls timed with HIP events on the launch
     stream; GB/s on the algorithmic bytes 5(R-1)N."""
     import workloads
@@ -470,7 +470,7 @@ def r16_sweep(rr, torch, np, layout="separate"):
             ranks[r].copy_(torch.from_numpy(x[r]))
         del x
         restore = restore()
-        for op, ns in (("sum", 1), ("sum", 4), ("sum", 16), ("max", 4)):
+        for op, ns in (("sum", 1), ("sum", 2), ("sum", 4), ("sum", 8), ("sum", 16), ("max", 4)):
             for sync in ("barrier", "p2p"):
                 p = rr.plan(w0.R, w0.count, "fp32", ns, sync=sync)
                 restore()
