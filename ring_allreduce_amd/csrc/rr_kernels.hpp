@@ -27,6 +27,7 @@ struct LaunchTag {
     uint64_t* exits;  // workgroups of the running launch that have left
 };
 
+// The in-place ring (one launch runs hops g_first..g_last).
 struct RingArgs {
     void* bufs[RR_MAX_RANKS];
     uint64_t count;      // elements per rank
@@ -65,6 +66,7 @@ constexpr int kA2AUnroll = 8;
 constexpr int kCopyBlock = 1024;
 constexpr int kCopyPerCU = 2;
 constexpr int kA2AWavesPerCU = 16;
+// What a staged launch computes.
 enum : int { MODE_ALLREDUCE = 0, MODE_RS = 1, MODE_AG = 2 };
 
 struct StagedArgs {
@@ -160,10 +162,10 @@ __device__ __forceinline__ int wrap(int a, int m) {
     return r < 0 ? r + m : r;
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin by index.  Both kernels lay
-// their grid out as columns of R workgroups (one per rank) with every column on
-// one XCD: block b = ((col / 8) * R + rank) * 8 + col % 8.  Column counts are
-// padded to a multiple of 8; padding columns exit at once.
+// Workgroups are dealt to the 8 XCDs round-robin by index.  The ring, staged and
+// barrier kernels lay their grid out as columns of R workgroups (one per rank)
+// with every column on one XCD: block b = ((col / 8) * R + rank) * 8 + col % 8.
+// Column counts are padded to a multiple of 8; padding columns exit at once.
 struct Place {
     int rank;
     int col;

@@ -19,7 +19,11 @@
 // consumer advances its shadow by 1 and waits (P2P); or, for a per-hop barrier,
 // every workgroup of the lane adds 1 to all R-1 other ranks' signals and each
 // waiter advances its shadow by R-1 (the counting barrier of the DeepEP pull
-// request "make the rail barrier a counting barrier", section "Fix").
+// request "make the rail barrier a counting barrier", section "Fix").  A
+// workgroup serves `depth` lanes interleaved hop by hop (one lane's hand-off
+// completes while the other's hop runs) and `rounds` groups of lanes one after
+// another (so that the lanes in flight keep a hop's partials cached until the
+// next hop reads them).
 //
 // One producer per rank per signal is what makes the count safe to hand data
 // over.  Had the W workgroups of a slice shared one signal, a workgroup running
