@@ -141,7 +141,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the virtual ranks of the ring all live in one "
-              "MI355X's HBM, and this build runs nothing across GPUs. Use --gpus 1.",
+              "MI355X's HBM, and the library has no path across GPUs. Use --gpus 1.",
               file=sys.stderr, flush=True)
         return 2
 

@@ -235,3 +235,13 @@ def test_timed_barrier_run_validates_on_host(rr):
     assert rr._cb_run_timed(fake, 2, 1, 1, 1, None, None, ctypes.byref(khz), None) == \
         rr.RR_ERR_INVALID
     assert rr._cb_run_timed(fake, 2, 1, 1, 1, None, A, None, None) == rr.RR_ERR_INVALID
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with a message and status 2."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    run = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=root)
+    assert run.returncode == 2
+    assert "one GPU" in run.stdout + run.stderr
