@@ -434,7 +434,10 @@ const char *rr_status_string(rr_status_t s);
 /* RR_ABI_VERSION of the loaded library. */
 int rr_abi_version(void);
 
-/* Frees every device's workspace.  No call may be in flight. */
+/* Frees every device's workspace (and the staged loop's receive buffers).  No
+   call may be in flight, and a graph captured before must not be replayed after:
+   its launches hold the freed addresses.  The next call on a device creates a
+   fresh workspace, as the first one did. */
 void rr_finalize(void);
 
 #ifdef __cplusplus
