@@ -473,8 +473,8 @@ def test_full_r8_fp32_64MiB(rr):
     _full_size(rr, workloads.R8_FP32_64MIB, 20000)
 
 
-@pytest.mark.parametrize("w", [workloads.R8_FP32_64MIB, workloads.R64_FP32_32MIB],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [workloads.R8_FP32_64MIB, workloads.R8_BF16_256MIB,
+                               workloads.R64_FP32_32MIB], ids=lambda w: w.name)
 def test_full_size_in_the_bench_layout(rr, w):
     """The timed configuration itself: one tensor per rank from bench.py's own
     buffer helper and the call bench.py times (same options), checked at sampled
@@ -485,16 +485,18 @@ def test_full_size_in_the_bench_layout(rr, w):
     p = rr.plan(w.R, w.count, w.dtype, w.nslices, **opts)
     log(f"case bench layout {w.name} plan={p}")
     x = workloads.inputs(w)
-    ranks, snapshot = bench.rank_buffers(rr, torch, w.R, w.count, torch.float32, "separate")
+    tdt, raw_t, raw_np = ((torch.bfloat16, torch.int16, np.int16) if w.dtype == "bf16"
+                          else (torch.float32, torch.int32, np.int32))
+    ranks, snapshot = bench.rank_buffers(rr, torch, w.R, w.count, tdt, "separate")
     for r in range(w.R):
-        ranks[r].view(torch.int32).copy_(torch.from_numpy(x[r].view(np.int32)))
+        ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
     restore = snapshot()
     rr.allreduce_ring(ranks, w.op, w.nslices, **opts)
     torch.cuda.synchronize()
     rr.check_kernel_error()
     first = [t.clone() for t in ranks]
     for r in range(1, w.R):
-        assert torch.equal(first[r].view(torch.int32), first[0].view(torch.int32))
+        assert torch.equal(first[r].view(raw_t), first[0].view(raw_t))
     pos = sample_positions(w.count, w.R, w.dtype, w.nslices, p, 5000, w.seed)
     idx = torch.from_numpy(pos).cuda()
     got = np.stack([to_host(t.index_select(0, idx), w.dtype) for t in first], axis=1)
@@ -506,7 +508,7 @@ def test_full_size_in_the_bench_layout(rr, w):
     torch.cuda.synchronize()
     rr.check_kernel_error()
     for r in range(w.R):
-        assert torch.equal(ranks[r].view(torch.int32), first[r].view(torch.int32))
+        assert torch.equal(ranks[r].view(raw_t), first[r].view(raw_t))
 
 
 def test_full_r8_bf16_256MiB(rr):
