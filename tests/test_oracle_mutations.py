@@ -65,6 +65,11 @@ MUTANTS = [
     ("staged_reduces_in_allgather", "reduce = k >= 1 && k <= R - 1;", "reduce = k >= 1;", 0),
     ("ag_nccl_skips_own_block", "has_out = 1;", "has_out = k >= 1;", 0),
     ("bf16_nan_payload", "if (isnan(x)) return 0x7FC0u;", "if (isnan(x)) return 0x7FC1u;", 0),
+    ("direct_sum_float_accumulator", "double s = 0.0, a = 0.0;", "float s = 0.0f, a = 0.0f;", 0),
+    ("direct_sum_abs_without_fabs", "a += fabs(x);", "a += x;", 0),
+    ("direct_sum_decodes_bf16_as_fp16", ": dt == RO_BF16 ?", ": dt == RO_FP16 ?", 0),
+    ("direct_sum_drops_a_rank", "for (int r = 0; r < R; ++r) {\n            double x", "for (int r = 1; r < R; ++r) {\n            double x", 0),
+    ("fp16_decode_subnormal_scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);", 0),
     ("ag_reduces", "memcpy((char *)bufs[q] + lo * es, (const char *)bufs[r] + lo * es, n * es);",
      "fold_range(dt, RO_MAX, (const char *)bufs[r] + lo * es, (char *)bufs[q] + lo * es, n);", 0),
 ]
@@ -93,6 +98,13 @@ def _pin_suite():
         lambda: pins.test_all_gather_is_a_bit_copy("fp32", 5),
         lambda: pins.test_reduce_scatter_then_all_gather("fp32", "sum", 3),
         pins.test_reduce_scatter_partials,
+        lambda: pins.test_direct_sum_decodes_every_16bit_pattern("bf16"),
+        lambda: pins.test_direct_sum_decodes_every_16bit_pattern("fp16"),
+        pins.test_direct_sum_decodes_fp32_patterns,
+        lambda: pins.test_direct_sum_is_the_exact_sum("fp32", "uniform_pm1", 3),
+        lambda: pins.test_direct_sum_keeps_far_apart_terms("fp32", 0x30800000),
+        lambda: pins.test_direct_sum_keeps_far_apart_terms("fp16", 0x0001),
+        pins.test_direct_sum_special_values,
         lambda: pins.test_partition(10, 4, "fp32"),
         lambda: pins.test_partition(100, 8, "bf16"),
         pins.test_edge_cases,

@@ -9,8 +9,10 @@
   AllReduce, per-rank traffic equals the post's 2N(k-1)/k (section 13);
 * the floating-point error bounds that the ring's fold order must meet.
 """
+import math
 import os
 import random
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -413,3 +415,139 @@ def test_allreduce_at_matches_full_run(dtype, op):
     for k, p in enumerate(pos):
         for r in range(R):
             assert _bits(got[k:k + 1, r], dtype)[0] == _bits(full[r][p:p + 1], dtype)[0]
+
+
+# ------------------------------------------- the order-free reference sum
+# ro_direct_sum_f64 gives, per element, the sum of the ranks' values and of
+# their magnitudes, accumulated in binary64 in rank order.  It is the expected
+# value of every floating-point tolerance check (the ring post, section 1: the
+# AllReduce result is the reduction over all ranks), so it is pinned here to
+# the formats' own decoding, to exact rational sums and to math.fsum.
+
+def _decode_exact(bits, dtype):
+    """Exact value of one pattern: a Fraction, or a float for zero, inf, NaN."""
+    if dtype == "bf16":
+        return brute.bf16_bits_to_value(int(bits))
+    if dtype == "fp16":
+        return brute.fp16_bits_to_value(int(bits))
+    return brute.fp32_bits_to_value(int(bits))
+
+
+def _as_float(v):
+    return v if isinstance(v, float) else float(v)
+
+
+def _raw(dtype, bits):
+    bits = np.asarray(bits)
+    if dtype == "bf16":
+        return bits.astype(np.uint16)
+    if dtype == "fp16":
+        return bits.astype(np.uint16).view(np.float16)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_direct_sum_decodes_every_16bit_pattern(dtype):
+    """One rank: the sum is the pattern's value and the magnitude sum its
+    absolute value, for all 65536 patterns (subnormals, infinities and NaNs
+    included), each decoded exactly by the brute-force module."""
+    x = _raw(dtype, np.arange(1 << 16))
+    s, a = oracle.direct_sum_f64([x])
+    for bits in range(1 << 16):
+        v = _decode_exact(bits, dtype)
+        if isinstance(v, float) and v != v:
+            assert np.isnan(s[bits]) and np.isnan(a[bits]), hex(bits)
+            continue
+        want = _as_float(v)
+        assert s[bits] == want and a[bits] == abs(want), (hex(bits), s[bits], want)
+
+
+def test_direct_sum_decodes_fp32_patterns():
+    """One rank, binary32: subnormals, the extremes, specials and random bits."""
+    rnd = random.Random(12)
+    pats = [0x00000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0x80000001, 0xFF7FFFFF, 0x3F800000,
+            0x7F800000, 0xFF800000, 0x7FC00001, 0x80000000] + [rnd.getrandbits(32) for _ in range(4000)]
+    x = _raw("fp32", pats)
+    s, a = oracle.direct_sum_f64([x])
+    for k, bits in enumerate(pats):
+        v = _decode_exact(bits, "fp32")
+        if isinstance(v, float) and v != v:
+            assert np.isnan(s[k])
+            continue
+        assert s[k] == _as_float(v) and a[k] == abs(_as_float(v)), hex(bits)
+
+
+@pytest.mark.parametrize("dtype,dist,R", [("fp32", "uniform_pm1", 64), ("bf16", "normal", 8),
+                                          ("fp16", "normal", 8), ("fp32", "uniform_pm1", 3)])
+def test_direct_sum_is_the_exact_sum(dtype, dist, R):
+    """On the workloads' value distributions every partial sum fits binary64's
+    53 bits, so the result must be the exact rational sum (checked to be
+    representable first), and equal to math.fsum; the magnitude sum likewise."""
+    count = 700
+    x = workloads.generate(R, count, dtype, dist, 77 + R)
+    s, a = oracle.direct_sum_f64(x)
+    raw = [v.view(np.uint16) if dtype != "fp32" else v.view(np.uint32) for v in x]
+    for i in range(count):
+        vals = [_decode_exact(raw[r][i], dtype) for r in range(R)]
+        fr = [v if not isinstance(v, float) else Fraction(0) for v in vals]
+        exact = sum(fr, Fraction(0))
+        mag = sum((abs(v) for v in fr), Fraction(0))
+        assert Fraction(float(exact)) == exact and Fraction(float(mag)) == mag
+        assert s[i] == float(exact), (i, s[i], float(exact))
+        assert a[i] == float(mag)
+        assert s[i] == math.fsum(float(v) for v in fr)
+
+
+@pytest.mark.parametrize("dtype,small", [("fp32", 0x30800000), ("bf16", 0x3080), ("fp16", 0x0001)])
+def test_direct_sum_keeps_far_apart_terms(dtype, small):
+    """1 + tiny - 1 with tiny far below the format's unit at 1 (2^-30, or
+    binary16's smallest subnormal 2^-24): exact in binary64, lost by any
+    narrower accumulator; 1 - 1 + tiny gives the same; magnitudes add."""
+    one, mone = {"fp32": (0x3F800000, 0xBF800000), "bf16": (0x3F80, 0xBF80),
+                 "fp16": (0x3C00, 0xBC00)}[dtype]
+    tiny = _as_float(_decode_exact(small, dtype))
+    for order in ((one, small, mone), (one, mone, small)):
+        x = [_raw(dtype, [b]) for b in order]
+        s, a = oracle.direct_sum_f64(x)
+        assert s[0] == tiny and a[0] == 2.0 + tiny
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_direct_sum_within_the_summation_bound(dtype):
+    """Random patterns over the whole finite range, 16 ranks: within the
+    recursive-summation bound (R-1) 2^-53 sum|x| of math.fsum (whose result is
+    the correctly rounded sum), for the sum and the magnitude sum."""
+    rng = np.random.default_rng(3)
+    R, count = 16, 2000
+    nbits = 32 if dtype == "fp32" else 16
+    x = []
+    for _ in range(R):
+        bits = rng.integers(0, 1 << nbits, size=count, dtype=np.uint64)
+        v = _raw(dtype, bits)
+        f = v.astype(np.float64) if dtype != "bf16" else \
+            (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ok = np.isfinite(f)
+        bits = np.where(ok, bits, 0)
+        x.append(_raw(dtype, bits))
+    s, a = oracle.direct_sum_f64(x)
+    raw = [v.view(np.uint16) if dtype != "fp32" else v.view(np.uint32) for v in x]
+    gamma = (R - 1) * 2.0 ** -53
+    for i in range(count):
+        vals = [_as_float(_decode_exact(raw[r][i], dtype)) for r in range(R)]
+        fs = math.fsum(vals)
+        fa = math.fsum(abs(v) for v in vals)
+        if math.isinf(fs) or math.isinf(fa):
+            continue
+        assert abs(s[i] - fs) <= gamma * fa * (1 + 1e-12), (i, s[i], fs)
+        assert abs(a[i] - fa) <= gamma * fa * (1 + 1e-12)
+
+
+def test_direct_sum_special_values():
+    """An infinity makes the sum infinite, opposite infinities or a NaN make it
+    NaN; the magnitude sum is infinite in every case but NaN."""
+    inf, ninf, nan, one = 0x7F800000, 0xFF800000, 0x7FC00000, 0x3F800000
+    cols = [(inf, one), (inf, ninf), (nan, one), (ninf, ninf)]
+    x = [_raw("fp32", [c[r] for c in cols]) for r in range(2)]
+    s, a = oracle.direct_sum_f64(x)
+    assert s[0] == np.inf and np.isnan(s[1]) and np.isnan(s[2]) and s[3] == -np.inf
+    assert a[0] == np.inf and a[1] == np.inf and np.isnan(a[2]) and a[3] == np.inf
