@@ -1,25 +1,36 @@
 """Benchmark: ring AllReduce over R virtual ranks on one MI355X.
 
-Default workload: R=8 virtual ranks, fp32, 64 MiB per rank, SUM, 4 slices.  One
-step is one in-place AllReduce call (2(R-1) ring hops) over all R rank buffers,
-inputs resident in HBM.  The rank buffers are separate tensors, as a caller's
-are (--layout slab carves them from one allocation instead, 256 bytes apart:
-R=64 in barrier mode runs about 4% slower there).
+Default workload: R=16 virtual ranks, fp32, 1 GiB per rank, SUM, 16 slices,
+counting-barrier step sync (every rank adds 1 to each other rank's signal of the
+lane after each hop; each waiter expects R-1).  One step is one in-place
+AllReduce call (2(R-1) ring hops) over all R rank buffers, inputs resident in
+HBM.  The rank buffers are separate tensors, as a caller's are (--layout slab
+carves them from one allocation instead, 256 bytes apart).
+
+Timing: W untimed calls, then exactly K timed calls.  Before every call the
+inputs are restored from a pristine device copy, outside that call's pair of
+HIP events on the launch stream, so every timed call reduces the workload's own
+data.  ms_per_step is the median of the K per-call times.
 
 value = algorithmic HBM bytes per call / time per call, with the algorithmic
 bytes of the in-place ring: each ReduceScatter hop reads the incoming and local
 chunk and writes the folded one (3 chunk transfers), each AllGather hop reads and
 writes one chunk (2), so B = 5 (R-1) N for N bytes per rank.
 
-Prints one JSON line (rank 0).  Also reports:
-  roofline      -- the ring kernel against MI355X's 8 TB/s HBM peak: its average
-                   launch duration from HIP events on the launch stream around the
-                   timed region; `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE
-                   record in profiles/ when it was taken on this kernel source;
-  cpu_baseline  -- the single-threaded CPU oracle on the same inputs (test
-                   infrastructure; timed only, never on the product path), which
-                   also cross-checks one GPU call;
-  copy_ceiling  -- the library's streaming copy kernel over 1 GiB + 1 GiB.
+Prints one JSON line.  Also reports:
+  roofline         -- the ring kernel against MI355X's 8 TB/s HBM peak: its
+                      average launch duration (the mean per-call event time over
+                      the timed calls); `traffic` from the rocprofv3
+                      FETCH_SIZE/WRITE_SIZE record in profiles/ when it was taken
+                      on this kernel source, with the rate those counter bytes
+                      give; the fraction of the same run's copy ceiling;
+  extra_workloads  -- the other benchmark workloads (R=8 fp32 64 MiB, R=8 bf16
+                      256 MiB, R=64 fp32 32 MiB), timed the same way;
+  cpu_baseline     -- the single-threaded CPU oracle on the same inputs (test
+                      infrastructure; timed only, never on the product path),
+                      whose result is compared with the last timed GPU call,
+                      every element of every rank;
+  copy_ceiling     -- the library's streaming copy kernel over 1 GiB + 1 GiB.
 """
 from __future__ import annotations
 
@@ -36,6 +47,8 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) for ring AllReduce over R virtual ranks"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+# timed after the headline in the same run (ring path), each with its own plan
+EXTRA_WORKLOADS = ("r8_fp32_64MiB", "r8_bf16_256MiB", "r64_fp32_32MiB")
 
 
 def log(msg):
@@ -47,9 +60,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="r8_fp32_64MiB",
-                    help="r8_fp32_64MiB | r8_bf16_256MiB | r64_fp32_32MiB | worked_example | "
-                         "r16_sweep:K[:op[:nslices]]")
+    ap.add_argument("--workload", default="r16_fp32_1GiB",
+                    help="r16_fp32_1GiB | r8_fp32_64MiB | r8_bf16_256MiB | r64_fp32_32MiB | "
+                         "worked_example | r16_sweep:K[:op[:nslices]]")
     ap.add_argument("--sync", default=None, help="auto | p2p | barrier | launch")
     ap.add_argument("--team", type=int, default=0)
     ap.add_argument("--block", type=int, default=0)
@@ -68,6 +81,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other benchmark workloads (ring path only)")
     ap.add_argument("--r16-sweep", action="store_true",
                     help="R=16 fp32 size sweep, 4 KiB .. 1 GiB per rank: one JSON line per point")
     ap.add_argument("--barrier-latency", action="store_true",
@@ -137,6 +152,199 @@ def stored_traffic(workload_name, digest):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _torch_types(torch, np, dtype):
+    tdt = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16,
+           "fp16": torch.float16}[dtype]
+    two = dtype in ("bf16", "fp16")
+    return tdt, (torch.int16 if two else torch.int32), (np.int16 if two else np.int32)
+
+
+class Run:
+    """One workload on one path: the rank buffers filled from the seeded inputs,
+    a pristine copy of them, and the call that makes one step."""
+
+    def __init__(self, rr, torch, np, w, path, opts, layout):
+        import workloads
+        self.rr, self.torch, self.w, self.path = rr, torch, w, path
+        self.blk = w.count // w.R
+        t = time.time()
+        self.x = workloads.inputs(w)
+        log(f"{w.name}: inputs generated in {time.time() - t:.1f} s")
+        tdt, raw_t, raw_np = _torch_types(torch, np, w.dtype)
+        self.raw_t, self.raw_np = raw_t, raw_np
+        ranks, snapshot = rank_buffers(rr, torch, w.R, w.count, tdt, layout)
+        for r in range(w.R):
+            ranks[r].view(raw_t).copy_(torch.from_numpy(self.x[r].view(raw_np)))
+        self.ranks = ranks
+        # in place (the ring): every call must start from the inputs again
+        self.restore = snapshot() if path == "ring" else (lambda: None)
+        blk = self.blk
+        if path == "ring":
+            self.out = ranks
+            self.call = lambda: rr.allreduce_ring(ranks, w.op, w.nslices, **opts)
+        elif path == "staged":
+            self.out = [torch.empty(w.count, dtype=tdt, device="cuda") for _ in range(w.R)]
+            self.call = lambda: rr.allreduce_ring_staged(ranks, self.out, w.op, w.nslices, **opts)
+        elif path == "reduce_scatter":
+            self.out = [torch.empty(blk, dtype=tdt, device="cuda") for _ in range(w.R)]
+            self.call = lambda: rr.reduce_scatter(ranks, self.out, w.op, w.nslices, **opts)
+        elif path == "all_gather":
+            send = [t[:blk] for t in ranks]
+            self.out = [torch.empty(w.count, dtype=tdt, device="cuda") for _ in range(w.R)]
+            self.call = lambda: rr.all_gather(send, self.out, w.nslices, **opts)
+        else:
+            self.out = [torch.empty(w.count, dtype=tdt, device="cuda") for _ in range(w.R)]
+            self.call = lambda: rr.alltoall(ranks, self.out)
+
+    def time(self, steps, warmup):
+        """W untimed calls, then exactly K timed calls.  Before every call the
+        inputs are restored from the pristine copy, outside that call's pair of
+        HIP events (recorded on the launch stream); the output left behind is
+        that of the last timed call, made from the inputs like every other."""
+        torch, rr = self.torch, self.rr
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            self.restore()
+            self.call()
+        torch.cuda.synchronize()
+        rr.check_kernel_error()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            self.restore()
+            e0.record(stream)
+            self.call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        rr.check_kernel_error()
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        srt = sorted(ms)
+        return {"calls": len(ms), "median_ms": round(srt[len(srt) // 2], 5),
+                "mean_ms": round(sum(ms) / len(ms), 5), "min_ms": round(srt[0], 5),
+                "max_ms": round(srt[-1], 5), "wall_s": round(wall, 3)}, ms
+
+    def release(self):
+        self.ranks = self.out = self.x = self.call = self.restore = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def _phase(path):
+    return {"ring": "allreduce", "staged": "allreduce_staged",
+            "reduce_scatter": "reduce_scatter_blocks", "all_gather": "all_gather_blocks",
+            "alltoall": "alltoall"}[path]
+
+
+def _plan_for(rr, w, path, opts):
+    n = w.count // w.R if path in ("reduce_scatter", "all_gather", "alltoall") else w.count
+    return rr.plan(w.R, n, w.dtype, w.nslices, phase=_phase(path),
+                   **({} if path == "alltoall" else opts))
+
+
+def _opts_for(w, path, args):
+    opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags,
+                fused=args.fused)
+    if path != "ring":
+        if w.sync == "barrier":
+            opts["sync"] = "auto"  # the staged loop is paced by its credits
+        opts.pop("fused")
+    return opts
+
+
+def copy_ceiling(rr, torch):
+    """The library's streaming copy over 1 GiB -> 1 GiB, and torch's elementwise
+    add over 1 GiB fp32 operands (2 reads + 1 write, the shape of a
+    ReduceScatter hop) as a reference."""
+    stream = torch.cuda.current_stream()
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        rr.hbm_copy(dst, src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    reps = 10
+    for _ in range(reps):
+        rr.hbm_copy(dst, src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    out = {"bytes": 2 * n, "ms": round(ms, 4), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    fa = src.view(torch.float32)
+    fb = dst.view(torch.float32)
+    fc = torch.empty_like(fa)
+    for _ in range(3):
+        torch.add(fa, fb, out=fc)
+    a.record(stream)
+    for _ in range(reps):
+        torch.add(fa, fb, out=fc)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms2 = a.elapsed_time(b) / reps
+    out["read2_write1"] = {"bytes": 3 * n, "ms": round(ms2, 4),
+                           "GB/s": round(3 * n / (ms2 * 1e-3) / 1e9, 1),
+                           "kernel": "torch.add (reference)"}
+    del src, dst, fc
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(run, np, budget_s):
+    """The oracle (test infrastructure, this leg only) on the same inputs: timed
+    on one host core over whole calls until the budget is spent (at least one
+    call), each call on a fresh copy of the inputs (the copy is not timed).  Its
+    result is then compared with the GPU output of the last timed call, every
+    element of every rank, one piece of each rank buffer at a time."""
+    import oracle
+    w, path, x = run.w, run.path, run.x
+    blk = run.blk
+    runs, spent, expect = 0, 0.0, None
+    work = None
+    while runs == 0 or spent < budget_s:
+        if path == "ring":
+            if work is None:
+                work = [np.empty_like(a) for a in x]
+            for a, b in zip(work, x):
+                np.copyto(a, b)
+            t = time.perf_counter()
+            oracle.allreduce(work, w.op)
+            spent += time.perf_counter() - t
+            expect = work
+        else:
+            t = time.perf_counter()
+            if path == "staged":
+                expect, _ = oracle.staged_allreduce(x, w.op)
+            elif path == "reduce_scatter":
+                expect, _ = oracle.reduce_scatter_nccl(x, w.op)
+            elif path == "alltoall":
+                expect = oracle.alltoall(x)
+            else:
+                expect, _ = oracle.all_gather_nccl([np.ascontiguousarray(a[:blk]) for a in x])
+            spent += time.perf_counter() - t
+        runs += 1
+    per = spent / runs
+    # every element of every rank, a piece at a time (bounded host memory)
+    piece = 1 << 26
+    ok = True
+    for r in range(w.R):
+        dev = run.out[r].view(run.raw_t)
+        want = expect[r].view(run.raw_np)
+        for lo in range(0, want.size, piece):
+            hi = min(lo + piece, want.size)
+            got = dev[lo:hi].cpu().numpy()
+            if not np.array_equal(got, want[lo:hi]):
+                ok = False
+                break
+        if not ok:
+            break
+    return per, runs, spent, ok
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -149,7 +357,6 @@ def main():
     import torch
 
     import ring_allreduce_amd as rr
-    import workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -162,197 +369,83 @@ def main():
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
-    opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags,
-                fused=args.fused)
     path = args.path
-    if path != "ring":
-        if w.sync == "barrier":
-            opts["sync"] = "auto"  # the staged loop is paced by its credits
-        opts.pop("fused")
-        if w.count % w.R:
-            print("the standalone collectives need a per-rank count divisible by R",
-                  file=sys.stderr)
-            return 2
-    blk = w.count // w.R
+    opts = _opts_for(w, path, args)
+    if path != "ring" and w.count % w.R:
+        print("the standalone collectives need a per-rank count divisible by R", file=sys.stderr)
+        return 2
     rr.init()
-    phase = {"ring": "allreduce", "staged": "allreduce_staged",
-             "reduce_scatter": "reduce_scatter_blocks", "all_gather": "all_gather_blocks",
-             "alltoall": "alltoall"}[path]
-    p = rr.plan(w.R, blk if path in ("reduce_scatter", "all_gather", "alltoall") else w.count,
-                w.dtype, w.nslices, phase=phase,
-                **({} if path == "alltoall" else opts))
+    p = _plan_for(rr, w, path, opts)
     log(f"workload {w.name} ({path}): R={w.R} {w.dtype} {w.op} "
         f"{w.bytes_per_rank / 2**20:.1f} MiB/rank nslices={w.nslices} plan={p}")
-
-    t = time.time()
-    x = workloads.inputs(w)
-    log(f"inputs generated in {time.time() - t:.1f} s")
-    torch_dt = {"int32": torch.int32, "fp32": torch.float32, "bf16": torch.bfloat16,
-                "fp16": torch.float16}[w.dtype]
-    raw_t = torch.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else torch.int32
-    raw_np = np.int16 if workloads.ELEM_BYTES[w.dtype] == 2 else np.int32
-    ranks, restore = rank_buffers(rr, torch, w.R, w.count, torch_dt, args.layout)
-    for r in range(w.R):
-        ranks[r].view(raw_t).copy_(torch.from_numpy(x[r].view(raw_np)))
-    restore = restore()  # snapshot the inputs; calling it copies them back
-    stream = torch.cuda.current_stream()
     kernel = {"ring": "ring_kernel", "alltoall": "alltoall_kernel"}.get(path, "staged_kernel")
 
-    if path == "ring":
-        out_bufs = ranks
-
-        def step():
-            rr.allreduce_ring(ranks, w.op, w.nslices, **opts)
-    elif path == "staged":
-        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
-
-        def step():
-            rr.allreduce_ring_staged(ranks, out_bufs, w.op, w.nslices, **opts)
-    elif path == "reduce_scatter":
-        out_bufs = [torch.empty(blk, dtype=torch_dt, device="cuda") for _ in range(w.R)]
-
-        def step():
-            rr.reduce_scatter(ranks, out_bufs, w.op, w.nslices, **opts)
-    elif path == "all_gather":
-        ag_send = [t[:blk] for t in ranks]
-        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
-
-        def step():
-            rr.all_gather(ag_send, out_bufs, w.nslices, **opts)
-    else:
-        out_bufs = [torch.empty(w.count, dtype=torch_dt, device="cuda") for _ in range(w.R)]
-
-        def step():
-            rr.alltoall(ranks, out_bufs)
-
-    # one checked call on the pristine inputs, kept for the CPU cross-check
-    step()
-    torch.cuda.synchronize()
-    rr.check_kernel_error()
-    first_result = [t.view(raw_t).cpu().numpy() for t in out_bufs]
-
-    for _ in range(args.warmup):
-        step()
-    restore()
-    torch.cuda.synchronize()
-    rr.check_kernel_error()
-
-    # timed region: exactly K steps
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    rr.check_kernel_error()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    run = Run(rr, torch, np, w, path, opts, args.layout)
+    timing, per_call = run.time(args.steps, args.warmup)
     B = p["hbm_bytes"]
+    ms_per_step = timing["median_ms"]
     value = B / (ms_per_step * 1e-3) / 1e9
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}) "
+    log(f"timed {args.steps} calls: median {ms_per_step:.4f} ms, mean {timing['mean_ms']:.4f} ms "
         f"-> {value:.1f} GB/s algorithmic")
 
-    # Per-call spread: each of K further calls between its own pair of events
-    # (outside the timed region above, so `value` is unaffected).
-    per_call_ms = []
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    rr.check_kernel_error()
-    per_call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    timing = {"calls": len(per_call_ms), "median_ms": round(per_call_ms[len(per_call_ms) // 2], 5),
-              "min_ms": round(per_call_ms[0], 5), "max_ms": round(per_call_ms[-1], 5)}
-
-    # The ring kernel's average launch duration: HIP events on the launch stream
-    # around the timed region, divided by the launches it holds (back to back).
-    per_call = p["launches"]
-    avg_launch_ms = ev0.elapsed_time(ev1) / (args.steps * per_call)
-    bytes_per_launch = B / per_call
+    # The kernel's average launch duration: the mean of the per-call HIP event
+    # times on the launch stream, divided by the launches one call makes.
+    per_call_launches = p["launches"]
+    avg_launch_ms = timing["mean_ms"] / per_call_launches
+    bytes_per_launch = B / per_call_launches
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     digest = source_digest()
     traffic = stored_traffic(w.name if path == "ring" else f"{path}_{w.name}", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kernel, "launch_ms_avg": round(avg_launch_ms, 5),
-                "launches_timed": args.steps * per_call, "bytes_per_launch": int(bytes_per_launch),
-                "kernel_source_digest": digest}
+                "launches_timed": args.steps * per_call_launches,
+                "bytes_per_launch": int(bytes_per_launch), "kernel_source_digest": digest}
+    if traffic:
+        # what the counters saw leave the L2s (Infinity Cache hits included)
+        cgbs = traffic / (avg_launch_ms * 1e-3) / 1e9
+        roofline["counter_GBps"] = round(cgbs, 1)
+        roofline["counter_frac"] = round(cgbs / HBM_PEAK_GBS, 4)
 
-    copy_ceiling = None
+    extra = {}
+    if path == "ring" and not args.no_extra:
+        for name in EXTRA_WORKLOADS:
+            if name == w.name:
+                continue
+            wx = workloads_all()[name]
+            ox = _opts_for(wx, "ring", args)
+            px = _plan_for(rr, wx, "ring", ox)
+            rx = Run(rr, torch, np, wx, "ring", ox, args.layout)
+            tx, _ = rx.time(args.steps, args.warmup)
+            rx.release()
+            bx = px["hbm_bytes"]
+            gbs = bx / (tx["median_ms"] * 1e-3) / 1e9
+            extra[name] = {"ms": tx["median_ms"], "mean_ms": tx["mean_ms"],
+                           "min_ms": tx["min_ms"], "max_ms": tx["max_ms"],
+                           "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "sync": px["sync"], "block": px["block"], "depth": px["depth"],
+                           "rounds": px["rounds"], "team": px["team"],
+                           "algorithmic_bytes": bx}
+            log(f"extra {name}: {extra[name]}")
+
+    ceiling = None
     if not args.no_copy_ceiling:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(3):
-            rr.hbm_copy(dst, src)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        reps = 10
-        for _ in range(reps):
-            rr.hbm_copy(dst, src)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        copy_ceiling = {"bytes": 2 * n, "ms": round(ms, 4),
-                        "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-        # a 2-read + 1-write stream (the shape of a ReduceScatter hop): torch's
-        # elementwise add over 1 GiB fp32 operands, as a reference only
-        fa = src.view(torch.float32)
-        fb = dst.view(torch.float32)
-        fc = torch.empty_like(fa)
-        for _ in range(3):
-            torch.add(fa, fb, out=fc)
-        a.record(stream)
-        for _ in range(reps):
-            torch.add(fa, fb, out=fc)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms2 = a.elapsed_time(b) / reps
-        copy_ceiling["read2_write1"] = {"bytes": 3 * n, "ms": round(ms2, 4),
-                                        "GB/s": round(3 * n / (ms2 * 1e-3) / 1e9, 1),
-                                        "kernel": "torch.add (reference)"}
-        del src, dst, fc
-        log(f"copy ceiling: {copy_ceiling}")
+        ceiling = copy_ceiling(rr, torch)
+        roofline["frac_of_copy_ceiling"] = round(achieved / ceiling["GB/s"], 4)
+        log(f"copy ceiling: {ceiling}")
 
-    cpu_baseline = None
+    cpu = None
     if not args.no_cpu_baseline:
-        import oracle  # test infrastructure: the CPU baseline leg only
-        runs, spent = 0, 0.0
-        expect = None
-        while runs == 0 or (spent < args.cpu_seconds and runs < 1000):
-            t = time.perf_counter()
-            if path == "ring":
-                bufs = [a.copy() for a in x]
-                t = time.perf_counter()
-                oracle.allreduce(bufs, w.op)
-            elif path == "staged":
-                bufs, _ = oracle.staged_allreduce(x, w.op)
-            elif path == "reduce_scatter":
-                bufs, _ = oracle.reduce_scatter_nccl(x, w.op)
-            elif path == "alltoall":
-                bufs = oracle.alltoall(x)
-            else:
-                bufs, _ = oracle.all_gather_nccl([np.ascontiguousarray(a[:blk]) for a in x])
-            spent += time.perf_counter() - t
-            runs += 1
-            expect = bufs
-        per = spent / runs
-        ok = all(np.array_equal(first_result[r].view(np.uint8), expect[r].view(np.uint8))
-                 for r in range(w.R))
-        cpu_baseline = {"value": round(B / per / 1e9, 3), "unit": "GB/s", "cores": 1,
-                        "kind": "oracle", "ms_per_call": round(per * 1e3, 1),
-                        "sample": f"the full {w.name} input, {runs} call(s) of the single-threaded "
-                                  f"C oracle ({spent:.1f} s)",
-                        "gpu_matches_oracle_bitwise": bool(ok),
-                        "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
-        log(f"cpu baseline: {cpu_baseline}")
+        per, runs, spent, ok = cpu_baseline(run, np, args.cpu_seconds)
+        cpu = {"value": round(B / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "ms_per_call": round(per * 1e3, 1),
+               "sample": f"the full {w.name} input, {runs} call(s) of the single-threaded C "
+                         f"oracle ({spent:.1f} s), each on a fresh copy of the inputs",
+               "gpu_matches_oracle_bitwise": bool(ok),
+               "compared": "every element of every rank: the output of the last timed call",
+               "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+        log(f"cpu baseline: {cpu}")
+    run.release()
 
     out = {
         "metric": METRIC if path == "ring" else f"{METRIC} ({path} path)",
@@ -366,15 +459,22 @@ def main():
                    "rounds": p["rounds"], "depth": p["depth"], "stream_loads": p["stream_loads"],
                    "fused_boundary": bool(p["fused"]) if path == "ring" else False,
                    "algorithmic_bytes_per_step": B, "layout": args.layout,
+                   "inputs_restored_before_each_call": path == "ring",
                    "parallelism": "virtual ranks on 1 GPU"},
         "timing": timing,
-        # ring traffic in the sources' sense: bytes sent over all links per call
+        # the ring's traffic in the sources' sense: bytes sent over all links per call
         "bus_bytes_per_step": (2 * (w.R - 1) * w.bytes_per_rank if path in ("ring", "staged")
                                else (w.R - 1) * w.bytes_per_rank),
-        "roofline": roofline, "cpu_baseline": cpu_baseline, "copy_ceiling": copy_ceiling,
+        "roofline": roofline, "cpu_baseline": cpu, "copy_ceiling": ceiling,
+        "extra_workloads": extra or None,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def workloads_all():
+    import workloads
+    return workloads.ALL
 
 
 def barrier_latency(rr, torch, np):
@@ -456,9 +556,10 @@ def barrier_latency(rr, torch, np):
 
 def r16_sweep(rr, torch, np, layout="separate"):
     """The R=16 fp32 sweep, 4 KiB * 4^k per rank (k = 0..9): SUM with 1, 2, 4, 8 and
-    16 slices and MAX with 4, each in barrier and p2p mode.  Per point: inputs
-    restored, 2 warm-up calls, then 10 calls timed with HIP events on the launch
-    stream; GB/s on the algorithmic bytes 5(R-1)N."""
+    16 slices and MAX with 4, each in barrier and p2p mode.  Per point: 2 warm-up
+    calls, then 10 calls, each after the inputs are restored (outside its events)
+    and timed with its own HIP events on the launch stream; the median is
+    reported.  GB/s on the algorithmic bytes 5(R-1)N."""
     import workloads
     rr.init()
     stream = torch.cuda.current_stream()
@@ -473,21 +574,24 @@ def r16_sweep(rr, torch, np, layout="separate"):
         for op, ns in (("sum", 1), ("sum", 2), ("sum", 4), ("sum", 8), ("sum", 16), ("max", 4)):
             for sync in ("barrier", "p2p"):
                 p = rr.plan(w0.R, w0.count, "fp32", ns, sync=sync)
-                restore()
                 for _ in range(2):
+                    restore()
                     rr.allreduce_ring(ranks, op, ns, sync=sync)
-                a = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(10):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(10)]
+                for a, e in evs:
+                    restore()
+                    a.record(stream)
                     rr.allreduce_ring(ranks, op, ns, sync=sync)
-                e.record(stream)
+                    e.record(stream)
                 torch.cuda.synchronize()
                 rr.check_kernel_error()
-                ms = a.elapsed_time(e) / 10
+                times = sorted(a.elapsed_time(e) for a, e in evs)
+                ms = times[len(times) // 2]
                 B = p["hbm_bytes"]
                 print(json.dumps({"metric": "R=16 fp32 sweep", "bytes_per_rank": w0.bytes_per_rank,
                                   "op": op, "nslices": ns, "sync": p["sync"], "ms": round(ms, 5),
+                                  "min_ms": round(times[0], 5),
                                   "GB/s": round(B / ms / 1e6, 1),
                                   "pct_of_peak": round(100 * B / ms / 1e6 / HBM_PEAK_GBS, 2),
                                   "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],

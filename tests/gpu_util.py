@@ -124,3 +124,27 @@ def oracle_at(x, pos, dtype, op):
     chunks = np.searchsorted(bounds, pos, side="right") - 1
     vals = np.stack([x[r][pos] for r in range(R)], axis=1)
     return oracle.allreduce_at(vals, chunks, dtype, op)
+
+
+def assert_full_matches(dev_ranks, expect, dtype, what="", piece=1 << 26):
+    """Every element of every rank buffer on the device against the expected host
+    arrays, bit for bit (fp32 NaNs compare equal whatever the payload), read back
+    one piece of each rank at a time so that host memory stays bounded."""
+    for r, (t, e) in enumerate(zip(dev_ranks, expect)):
+        want_all = e.view(RAW_NP[dtype])
+        assert t.numel() == want_all.size, f"{what}: rank {r} has {t.numel()} elements"
+        raw = t.view(RAW_TORCH[dtype])
+        for lo in range(0, want_all.size, piece):
+            hi = min(lo + piece, want_all.size)
+            got = raw[lo:hi].cpu().numpy().view(RAW_NP[dtype])
+            want = want_all[lo:hi]
+            if np.array_equal(got, want):
+                continue
+            eq = bits_equal(got, want, dtype)
+            if eq.all():
+                continue
+            bad = np.flatnonzero(~eq)
+            k = bad[0]
+            raise AssertionError(
+                f"{what}: rank {r} differs from the oracle at {bad.size} of {hi - lo} elements "
+                f"in [{lo}, {hi}); first at {lo + k}: got {got[k]:#x} want {want[k]:#x}")

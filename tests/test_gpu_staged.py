@@ -8,9 +8,9 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_util import (RAW_NP, assert_matches_oracle, bits_equal, guards_intact, log,
-                            oracle_at, oracle_expect, sample_positions, to_device, to_host,
-                            to_slabs)
+from tests.gpu_util import (RAW_NP, assert_full_matches, assert_matches_oracle, bits_equal,
+                            guards_intact, log, oracle_at, oracle_expect, sample_positions,
+                            to_device, to_host, to_slabs)
 
 pytestmark = pytest.mark.gpu
 
@@ -230,6 +230,9 @@ def test_staged_full_r8_fp32_64MiB(rr):
     got = np.stack([to_host(t.index_select(0, idx), w.dtype) for t in recv.ranks], axis=1)
     want = oracle_at(x, pos, w.dtype, w.op)
     assert bits_equal(got, want.view(got.dtype), w.dtype).all()
+    # every element of every rank
+    expect, _ = oracle.staged_allreduce(x, w.op)
+    assert_full_matches(recv.ranks, expect, w.dtype, "staged full")
 
 
 def test_reduce_scatter_full_size_unaligned(rr):

@@ -18,6 +18,9 @@ Workloads (sizes are per rank):
 * ``r8_bf16_256MiB`` -- R=8, bf16, 256 MiB, normal(0, 1), SUM, 8 slices.
 * ``r16_fp32_sweep`` -- R=16, fp32, 4 KiB * 4^k for k = 0..9 (4 KiB .. 1 GiB),
   uniform in [-1, 1), SUM and MAX, 1..16 slices, counting-barrier step sync.
+* ``r16_fp32_1GiB`` -- the largest point of that sweep as a workload of its own:
+  R=16, fp32, 1 GiB, uniform in [-1, 1), SUM, 16 slices, counting-barrier step
+  sync (the same inputs as sweep point k = 9).
 * ``r64_fp32_32MiB`` -- R=64, fp32, 32 MiB, uniform in [-1, 1), SUM, 8 slices
   as independent contexts, counting-barrier step sync (R-1 arrivals per step).
 """
@@ -71,7 +74,10 @@ def r16_sweep(k: int, op: str = "sum", nslices: int = 4) -> Workload:
                     nslices, 40 + k, "uniform_pm1", sync="barrier")
 
 
-ALL = {w.name: w for w in (WORKED_EXAMPLE, R8_FP32_64MIB, R8_BF16_256MIB, R64_FP32_32MIB)}
+R16_FP32_1GIB = r16_sweep(9, "sum", 16).with_(name="r16_fp32_1GiB")
+
+ALL = {w.name: w for w in (WORKED_EXAMPLE, R8_FP32_64MIB, R8_BF16_256MIB, R64_FP32_32MIB,
+                           R16_FP32_1GIB)}
 
 
 def _draw(dist: str, dtype: str, count: int, rank: int, seed: int) -> np.ndarray:
