@@ -72,7 +72,8 @@
  * device workspace and advances on the device, so a replay behaves as a fresh
  * call.  The staged loop's receive buffers must already be large enough (a
  * call of the same or larger size made outside capture), since growing them
- * allocates.
+ * allocates.  Growing them later does not free the smaller buffers (they are
+ * kept until rr_finalize), so a graph captured before a growth still replays.
  */
 #ifndef RR_H
 #define RR_H
@@ -210,9 +211,11 @@ typedef struct {
 } rr_plan_t;
 
 /* Device-side failure record (rr_last_kernel_error).  Following the DeepEP
-   pull request (section "Fix"), a counting signal cannot name the missing peer,
-   so the record gives the signal and how many arrivals were missing; only a
-   per-peer barrier (RR_SYNC_PER_PEER) can name the peer. */
+   pull request (section "Cost": with one counting slot the stalled peer cannot
+   be identified, so the timeout diagnostic gives the number of missing arrivals
+   and the signal), the record gives the waiter's signal (context and rank) and
+   expected - observed missing arrivals; only a per-peer barrier
+   (RR_SYNC_PER_PEER) can name the peer. */
 typedef struct {
     int32_t status;    /* RR_OK or RR_ERR_TIMEOUT */
     int32_t ctx;       /* context (lane = slice * team + member) of the waiter */
@@ -271,7 +274,8 @@ rr_status_t all_gather_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_
    (same chunks, same fold order).  recvbufs[r] == sendbufs[r] is allowed (in
    place); any other overlap is not.  Messages travel through library-owned
    receive buffers of two chunk-sized slots per rank (2 * count elements in
-   all, allocated on first use and grown on demand; not under stream capture),
+   all, allocated on first use and grown on demand, outgrown ones kept until
+   rr_finalize; not under stream capture),
    handed off by a `ready` signal per (lane, rank) and returned by a `credit`
    signal, so traffic is (6R - 4) * count * elem bytes instead of the in-place
    ring's 5(R - 1).  Options: sync AUTO, P2P or LAUNCH (BARRIER is
@@ -352,7 +356,10 @@ rr_status_t counting_barrier_reset(rr_counting_barrier_t *b, rr_stream_t stream)
 /* Presets every signal and shadow to `value` (wrap tests); quiescent only. */
 rr_status_t counting_barrier_preset(rr_counting_barrier_t *b, uint64_t value, rr_stream_t stream);
 
-/* Reads one waiter's signal and shadow, synchronously (waits for the device). */
+/* Reads one waiter's signal and shadow, synchronously (waits for the device):
+   the signal's current value, as the read method of the 2kiu.com article on NCCL
+   GIN (section "Signal methods") returns it, and the shadow the waiter keeps.
+   Errors: RR_ERR_INVALID (b NULL, ctx or waiter out of range), RR_ERR_HIP. */
 rr_status_t counting_barrier_read(rr_counting_barrier_t *b, int ctx, int waiter, uint64_t *value,
                                   uint64_t *shadow);
 
@@ -370,7 +377,10 @@ rr_status_t counting_barrier_early_passes(rr_counting_barrier_t *b, int ctx, int
                                           uint64_t *count);
 
 /* Runs `nsteps` barrier steps over the first `ncontexts` contexts with R
-   waiters each, one workgroup per (context, waiter), in one kernel.  Per step a
+   waiters each, one workgroup per (context, waiter), in one kernel: the counting
+   barrier of the DeepEP pull request (section "Fix": every peer adds 1 to the
+   waiter's one signal, the waiter advances its shadow by the expected arrivals
+   and polls that signal), or, for comparison, the layouts below.  Per step a
    waiter arrives (opt->sync RR_SYNC_BARRIER or AUTO: adds 1 to every other
    waiter's signal in its context; RR_SYNC_P2P: adds 1 to its successor's;
    RR_SYNC_PER_PEER: adds 1 to its own slot in every other waiter's row) and
@@ -406,7 +416,9 @@ rr_status_t counting_barrier_run_timed(rr_counting_barrier_t *b, int R, int nste
 
 /* ---------------------------------------------------------------- support */
 
-/* Waits for `stream`, then reports and clears the device's failure record.
+/* Waits for `stream`, then reports and clears the device's failure record: the
+   timeout diagnostic of the DeepEP pull request (section "Cost": how many of the
+   expected arrivals are missing, and at which signal).
    Returns RR_OK if no wait failed since the last call, else the recorded status
    (RR_ERR_TIMEOUT) with the record in *rec (rec may be NULL).  While a failure
    is recorded every ring and barrier kernel on the device returns at once

@@ -106,6 +106,7 @@ struct DeviceState {
     uint64_t* credit_shadow = nullptr;
     char* fifo = nullptr;               // staged loop: receive buffers, grown on demand
     size_t fifo_bytes = 0;
+    std::vector<void*> retired;         // receive buffers outgrown, kept until rr_finalize
     uint64_t* launch_gen = nullptr;     // per-launch tag of the XCD table (starts at 1)
     uint64_t* launch_exits = nullptr;   // workgroups of the running launch that have left
 };
@@ -584,17 +585,15 @@ static rr_status_t check_staged_args(const void* const* send, void* const* recv,
     return RR_OK;
 }
 
+// Grows the staged loop's receive buffers.  An outgrown buffer is not freed
+// until rr_finalize: kernels still queued, and launches captured earlier into a
+// HIP graph, hold its address.
 static rr_status_t ensure_fifo(DeviceState* d, size_t bytes) {
     std::lock_guard<std::mutex> lock(g_mu);
     if (d->fifo_bytes >= bytes) return RR_OK;
-    if (d->fifo) {
-        if (!hip_ok(hipDeviceSynchronize())) return RR_ERR_HIP;
-        (void)hipFree(d->fifo);
-        d->fifo = nullptr;
-        d->fifo_bytes = 0;
-    }
     void* p = nullptr;
     if (!hip_ok(hipMalloc(&p, bytes))) return RR_ERR_NOMEM;
+    if (d->fifo) d->retired.push_back(d->fifo);
     d->fifo = (char*)p;
     d->fifo_bytes = bytes;
     return RR_OK;
@@ -1150,6 +1149,7 @@ void rr_finalize(void) {
         (void)hipDeviceSynchronize();
         (void)hipFree(d.mem);
         if (d.fifo) (void)hipFree(d.fifo);
+        for (void* q : d.retired) (void)hipFree(q);
         (void)hipSetDevice(prev);
         d = DeviceState();
     }

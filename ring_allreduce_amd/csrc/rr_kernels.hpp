@@ -21,9 +21,11 @@ constexpr int kSlots = RR_MAX_SLICES * RR_MAX_RANKS;  // (context, rank) pairs
 // from a captured graph still gets a fresh one: every workgroup reads `gen` at
 // start, and the last workgroup to leave a launch advances it for the next
 // launch (launches on one device are ordered, so no launch starts before the
-// previous one has left).  Zero is never used: the table starts zeroed.
+// previous one has left).  Table entries carry a published bit, so a zeroed
+// table matches no tag, and zeroed memory (tag, exit count, table) is a valid
+// starting state.
 struct LaunchTag {
-    uint64_t* gen;    // current tag, in [1, 2^32)
+    uint64_t* gen;    // current tag (its low 32 bits)
     uint64_t* exits;  // workgroups of the running launch that have left
 };
 
@@ -36,7 +38,7 @@ struct RingArgs {
     uint64_t sub_len;    // nominal length per team member
     uint64_t* sig;       // signal of slot s at sig[s * kSignalStride]
     uint64_t* shadow;    // shadow of slot s
-    uint64_t* xcc_table; // per workgroup: (generation << 8) | XCC id, published at start
+    uint64_t* xcc_table; // per workgroup: (generation << 8) | published | XCC id, set at start
     ErrorRecord* err;
     uint64_t timeout_ticks;
     LaunchTag launch;    // per-launch tag of the XCD table (device side)
@@ -188,10 +190,12 @@ __device__ __forceinline__ uint32_t xcc_id() {
     return __builtin_amdgcn_s_getreg(20 /* HW_REG_XCC_ID */ | (0 << 6) | ((4 - 1) << 11));
 }
 
-// Every synchronising workgroup publishes (generation << 8) | XCC id at start.
+// Every synchronising workgroup publishes (generation << 8) | published | XCC id
+// at start.
+constexpr uint64_t kXccPublished = 0x80;
 __device__ __forceinline__ void publish_xcc(uint64_t* table, uint32_t generation, uint32_t xcc) {
-    __hip_atomic_store(&table[blockIdx.x], ((uint64_t)generation << 8) | xcc, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&table[blockIdx.x], ((uint64_t)generation << 8) | kXccPublished | xcc,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Called by wave 0.  1 when the R workgroups of column `col` all run on this
@@ -210,7 +214,7 @@ __device__ inline int column_on_one_xcd(const uint64_t* table, uint32_t generati
         uint64_t v = sig_read(e);
         const uint64_t start = wall_clock64();
         uint32_t spins = 0;
-        while ((uint32_t)(v >> 8) != generation) {
+        while ((uint32_t)(v >> 8) != generation || !(v & kXccPublished)) {
             __builtin_amdgcn_s_sleep(1);
             v = sig_read(e);
             if ((++spins & 31u) == 0u &&
@@ -219,7 +223,7 @@ __device__ inline int column_on_one_xcd(const uint64_t* table, uint32_t generati
                 break;
             }
         }
-        same = !failed && (uint32_t)(v & 0xFFu) == mine;
+        same = !failed && (uint32_t)(v & 0x7Fu) == mine;
     }
     if (__any(failed)) return -1;
     return __all(same) ? 1 : 0;

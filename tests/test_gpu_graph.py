@@ -159,3 +159,46 @@ def test_alltoall_replays(rr):
 
     _replay_and_check(rr, g, clear, lambda: [to_host(t, dtype) for t in recv], want, dtype,
                       "alltoall replay")
+
+
+def test_staged_replay_after_the_receive_buffers_grew(rr):
+    """A staged call captured while the receive buffers were small, replayed
+    after a larger eager call grew them (and after allocations that could have
+    taken the old buffers' memory): the replay still writes into buffers it
+    owns and matches the oracle, because outgrown receive buffers are kept until
+    rr_finalize."""
+    R, count, dtype = 8, 4 * 8192 + 3, "fp32"
+    log(f"case graph staged after growth R={R} count={count}")
+    rr.finalize()                            # start from no receive buffers at all
+    rr.init()
+    x = workloads.generate(R, count, dtype, "uniform_pm1", 16)
+    expect = oracle_expect(x, "sum")
+    send = to_slabs(rr, x, dtype)
+    recv = [torch.empty(count, dtype=torch.float32, device="cuda") for _ in range(R)]
+
+    def call():
+        rr.allreduce_ring_staged(send.ranks, recv, "sum", 4)
+
+    call()                                   # eager: receive buffers for this size
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    g = _capture(call)
+    big_n = 16 * count
+    xb = workloads.generate(R, big_n, dtype, "uniform_pm1", 17)
+    big_send = to_slabs(rr, xb, dtype)
+    big_recv = rr.allreduce_ring_staged(big_send.ranks, None, "sum", 4)  # grows them
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert_matches_oracle([to_host(t, dtype) for t in big_recv], oracle_expect(xb, "sum"), dtype,
+                          "the larger eager call")
+    del big_send, big_recv
+    fillers = [torch.full((count,), 7.0, device="cuda") for _ in range(4 * R)]
+
+    def clear():
+        for t in recv:
+            t.fill_(-1.0)
+
+    _replay_and_check(rr, g, clear, lambda: [to_host(t, dtype) for t in recv], expect, dtype,
+                      "staged replay after growth")
+    for t in fillers:                        # nothing wrote into other allocations
+        assert torch.all(t == 7.0)
