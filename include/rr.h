@@ -285,6 +285,26 @@ rr_status_t allreduce_ring_staged(const void *const *sendbufs, void *const *recv
                                   size_t count, rr_dtype_t dt, rr_op_t op, int nslices,
                                   const rr_options_t *opt, rr_stream_t stream);
 
+/* allreduce_ring_staged for callers that cannot allocate device memory: code
+   under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+   Same arguments, options, results (the same bits) and errors as
+   allreduce_ring_staged, but it never allocates: the receive slots, signals,
+   shadows and failure record live in a static device array of this library
+   (about 65 MiB on every device the library runs on, held until the process
+   ends), which every call on a device shares.  Limits: the receive slots hold
+   64 MiB, i.e. 2 * R * chunk bytes <= 64 MiB with chunk = ceil(count / R)
+   rounded up to a 16-byte vector (about count * elem <= 32 MiB), and a plan may
+   use at most 4096 (lane, rank) signal pairs (R * nslices <= 4096; the team is
+   chosen within it).  Beyond either limit the call returns RR_ERR_UNSUPPORTED
+   before enqueuing anything.  Calls that overlap in time on one device race on
+   the shared array: issue them on one stream or order them.  A wait that timed
+   out is reported by rr_last_kernel_error like any other, which allocates
+   nothing either. */
+rr_status_t allreduce_ring_staged_noalloc(const void *const *sendbufs, void *const *recvbufs,
+                                          int R, size_t count, rr_dtype_t dt, rr_op_t op,
+                                          int nslices, const rr_options_t *opt,
+                                          rr_stream_t stream);
+
 /* ReduceScatter with the standalone collective's numbering (the loosp.cn post,
    section 2: which rank keeps which reduced chunk is a matter of numbering).
    sendbufs[r] holds R blocks of recvcount elements, block q at element
@@ -416,7 +436,9 @@ rr_status_t counting_barrier_run_timed(rr_counting_barrier_t *b, int R, int nste
 
 /* ---------------------------------------------------------------- support */
 
-/* Waits for `stream`, then reports and clears the device's failure record: the
+/* Waits for `stream`, then reports and clears the device's failure record (that
+   of the library-owned workspace, else that of allreduce_ring_staged_noalloc's
+   static array; it allocates nothing): the
    timeout diagnostic of the DeepEP pull request (section "Cost": how many of the
    expected arrivals are missing, and at which signal).
    Returns RR_OK if no wait failed since the last call, else the recorded status
@@ -427,7 +449,8 @@ rr_status_t counting_barrier_run_timed(rr_counting_barrier_t *b, int R, int nste
 rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t *rec);
 
 /* Creates the current device's workspace now (so that later calls allocate
-   nothing).  Errors: RR_ERR_HIP, RR_ERR_NOMEM. */
+   nothing), and looks up the device address of allreduce_ring_staged_noalloc's
+   static array.  Errors: RR_ERR_HIP, RR_ERR_NOMEM. */
 rr_status_t rr_init(void);
 
 /* Presets every ring-workspace signal and shadow of the current device to

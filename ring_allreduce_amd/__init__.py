@@ -109,6 +109,8 @@ _all_gather_ring = _sig("all_gather_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i,
 _plan_query = _sig("rr_plan_query", _i, _i, _sz, _i, _i, _i, _OPT, ctypes.POINTER(_Plan))
 _allreduce_ring_staged = _sig("allreduce_ring_staged", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                               _i, _sz, _i, _i, _i, _OPT, _vp)
+_allreduce_ring_staged_noalloc = _sig("allreduce_ring_staged_noalloc", _i, ctypes.POINTER(_vp),
+                                      ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _OPT, _vp)
 _reduce_scatter = _sig("reduce_scatter", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i,
                        _i, _i, _OPT, _vp)
 _all_gather = _sig("all_gather", _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _sz, _i, _i,
@@ -136,6 +138,7 @@ _finalize = _sig("rr_finalize", None)
 # Every symbol include/rr.h declares, for the export check.
 EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
             "reduce_scatter_ring_ex", "all_gather_ring_ex", "allreduce_ring_staged",
+            "allreduce_ring_staged_noalloc",
             "reduce_scatter", "all_gather", "alltoall", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
             "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
@@ -282,6 +285,21 @@ def allreduce_ring_staged(send, recv=None, op: str = "sum", nslices: int = 1, *,
     return recv
 
 
+def allreduce_ring_staged_noalloc(send, recv, op: str = "sum", nslices: int = 1, *, stream=None,
+                                  **opts):
+    """allreduce_ring_staged without any device allocation by the library (its
+    receive slots and signals live in a static device array; the caller passes
+    the output tensors).  Returns recv."""
+    n = send[0].numel()
+    sp, rp, dt = _pair(send, recv, n, n)
+    with torch.cuda.device(send[0].device):
+        o = _options(**opts)
+        st = _allreduce_ring_staged_noalloc(sp, rp, len(send), n, DTYPES[dt], OPS[op], nslices,
+                                            ctypes.byref(o), _stream_handle(stream))
+    _check(st, "allreduce_ring_staged_noalloc")
+    return recv
+
+
 def reduce_scatter(send, recv=None, op: str = "sum", nslices: int = 1, *, stream=None, **opts):
     """Standalone ReduceScatter: send[r] holds R blocks; recv[r] gets block r
     reduced over all ranks.  Returns recv."""
@@ -345,6 +363,9 @@ def staged_ptrs(kind: str, send, recv, n: int, dtype, op="sum", nslices: int = 1
     opc = OPS.get(op, op if isinstance(op, int) else 99)
     if kind == "allreduce":
         return _allreduce_ring_staged(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
+    if kind == "allreduce_noalloc":
+        return _allreduce_ring_staged_noalloc(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o),
+                                              stream)
     if kind == "reduce_scatter":
         return _reduce_scatter(sp, rp, R, n, dt, opc, nslices, ctypes.byref(o), stream)
     if kind == "alltoall":

@@ -94,7 +94,8 @@ constexpr int kWideBarrierBlock = 1024;
 // ------------------------------------------------------------- host side --
 
 struct DeviceState {
-    bool ready = false;
+    bool info = false;    // attributes below read
+    bool ready = false;   // workspace allocated
     int cus = 0;
     int wall_khz = 0;
     uint64_t* mem = nullptr;
@@ -140,18 +141,33 @@ static size_t elem_bytes(int dt) { return dt == RR_BF16 || dt == RR_FP16 ? 2 : 4
 
 static bool hip_ok(hipError_t e) { return e == hipSuccess; }
 
+// The current device's attributes (compute units, wall-clock rate).  Allocates
+// nothing.  Call with g_mu held.
+static rr_status_t device_info_locked(int dev, DeviceState& d) {
+    if (d.info) return RR_OK;
+    if (!hip_ok(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)))
+        return RR_ERR_HIP;
+    if (!hip_ok(hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev)) ||
+        d.wall_khz <= 0)
+        d.wall_khz = 100000;  // the gfx9 constant-rate clock runs at 100 MHz
+    d.info = true;
+    return RR_OK;
+}
+
+static rr_status_t current_device(int* dev) {
+    if (!hip_ok(hipGetDevice(dev))) return RR_ERR_HIP;
+    if (*dev < 0 || *dev >= kMaxDevices) return RR_ERR_UNSUPPORTED;
+    return RR_OK;
+}
+
 static rr_status_t ensure_device(DeviceState** out) {
     int dev = 0;
-    if (!hip_ok(hipGetDevice(&dev))) return RR_ERR_HIP;
-    if (dev < 0 || dev >= kMaxDevices) return RR_ERR_UNSUPPORTED;
+    rr_status_t st = current_device(&dev);
+    if (st != RR_OK) return st;
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState& d = g_dev[dev];
     if (!d.ready) {
-        if (!hip_ok(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)))
-            return RR_ERR_HIP;
-        if (!hip_ok(hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev)) ||
-            d.wall_khz <= 0)
-            d.wall_khz = 100000;  // the gfx9 constant-rate clock runs at 100 MHz
+        if ((st = device_info_locked(dev, d)) != RR_OK) return st;
         // signals (one per cache line), shadows, the XCC table, the error record,
         // the staged loop's credit signals and their shadows, then the launch tag
         // and the exit count (a cache line each)
@@ -490,8 +506,11 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
 static int staged_last_step(int R, int mode) { return mode == MODE_ALLREDUCE ? 2 * R - 2 : R - 1; }
 
 // n: AllReduce elements per rank; ReduceScatter / AllGather elements per block.
+// slots: (lane, rank) signal slots available, which also bounds the grid (the
+// XCD table has one entry per slot).
 static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int dt, int op,
-                                    int nslices, int mode, const rr_options_t* opt, Plan* p) {
+                                    int nslices, int mode, const rr_options_t* opt, Plan* p,
+                                    int slots = kSlots) {
     const uint64_t es = elem_bytes(dt);
     const uint64_t V = 16 / es;
     const int requested = opt ? opt->sync : RR_SYNC_AUTO;
@@ -529,12 +548,13 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
         const uint64_t wanted = ceil_div((uint64_t)target_cols * rounds, (uint64_t)nslices);
         team = (int)std::max<uint64_t>(1, std::min<uint64_t>(by_size, wanted));
     }
-    const int max_team = std::max(1, kSlots / (R * nslices));
+    const int max_team = std::max(1, slots / (R * nslices));
     if (team > max_team) {
         if (opt && opt->team > 0) return RR_ERR_UNSUPPORTED;
         team = max_team;
     }
     const int lanes = nslices * team;
+    if ((int64_t)lanes * R > slots) return RR_ERR_UNSUPPORTED;
     if (lanes % rounds != 0 || rounds > lanes) {  // rounds must divide the lanes
         if (opt && opt->rounds > 0) return RR_ERR_UNSUPPORTED;
         while (rounds > 1 && lanes % rounds != 0) --rounds;
@@ -550,7 +570,7 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     p->grid = (int)(R * cols_launched);
     int sync = requested;
     if (sync == RR_SYNC_AUTO) sync = p->grid <= p->resident_max ? RR_SYNC_P2P : RR_SYNC_LAUNCH;
-    if (sync == RR_SYNC_P2P && (p->grid > p->resident_max || p->grid > kSlots))
+    if (sync == RR_SYNC_P2P && (p->grid > p->resident_max || p->grid > slots))
         return RR_ERR_UNSUPPORTED;
     p->sync = sync;
     p->launches = sync == RR_SYNC_LAUNCH ? p->g_last + 1 : 1;
@@ -610,13 +630,92 @@ static rr_status_t copy_bytes(void* dst, const void* src, uint64_t bytes, const 
     return hip_ok(hipGetLastError()) ? RR_OK : RR_ERR_HIP;
 }
 
+// ------------------------------------------ the staged loop without allocation
+//
+// allreduce_ring_staged_noalloc keeps everything the staged kernel needs beyond
+// the caller's buffers -- receive slots, ready and credit signals with their
+// shadows, the XCD table, the failure record, the launch tag -- in `scratch`, a
+// device array of fixed size in this library's code object.  Zeroed memory is a
+// valid starting state (every signal equals its shadow, no failure recorded,
+// table entries unpublished), so nothing is written at set-up.  In host code
+// `scratch` names a host-side stand-in; its device address, one per device, comes
+// from hipGetSymbolAddress and is the only address ever handed to a kernel.
+constexpr int kScratchSlots = 4096;                       // (lane, rank) pairs
+constexpr uint64_t kScratchFifoBytes = 64ull << 20;       // receive slots
+constexpr size_t kScratchFifoWords = kScratchFifoBytes / 8;
+constexpr size_t kScratchSignalWords = (size_t)kScratchSlots * kSignalStride;
+constexpr size_t kScratchWords = kScratchFifoWords          // receive slots (first: aligned)
+                                 + 2 * kScratchSignalWords  // ready and credit signals
+                                 + 2 * (size_t)kScratchSlots  // their shadows
+                                 + (size_t)kScratchSlots    // XCD table
+                                 + 16                       // failure record
+                                 + 2 * (size_t)kSignalStride;  // launch tag, exit count
+
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+struct Scratch {
+    char* fifo;
+    uint64_t* ready;
+    uint64_t* credit;
+    uint64_t* ready_shadow;
+    uint64_t* credit_shadow;
+    uint64_t* xcc_table;
+    ErrorRecord* err;
+    uint64_t* launch_gen;
+    uint64_t* launch_exits;
+};
+
+uint64_t* g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+static Scratch carve(uint64_t* base) {
+    Scratch c;
+    c.fifo = (char*)base;
+    c.ready = base + kScratchFifoWords;
+    c.credit = c.ready + kScratchSignalWords;
+    c.ready_shadow = c.credit + kScratchSignalWords;
+    c.credit_shadow = c.ready_shadow + kScratchSlots;
+    c.xcc_table = c.credit_shadow + kScratchSlots;
+    c.err = (ErrorRecord*)(c.xcc_table + kScratchSlots);
+    c.launch_gen = c.xcc_table + kScratchSlots + 16;
+    c.launch_exits = c.launch_gen + kSignalStride;
+    return c;
+}
+
+// Looks up the device address of `scratch` on the current device once (with
+// that device current) and keeps it.  Allocates nothing.  Call with g_mu held.
+static rr_status_t scratch_locked(int dev, uint64_t** out) {
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (!hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) || !p) {
+            (void)hipGetLastError();
+            return RR_ERR_HIP;
+        }
+        g_scratch[dev] = (uint64_t*)p;
+    }
+    *out = g_scratch[dev];
+    return RR_OK;
+}
+
 static rr_status_t run_staged(const void* const* send, void* const* recv, int R, uint64_t n, int dt,
                               int op, int nslices, int mode, const rr_options_t* opt,
-                              rr_stream_t stream) {
+                              rr_stream_t stream, bool noalloc = false) {
     rr_status_t st = check_staged_args(send, recv, R, n, dt, op, nslices, mode, opt);
     if (st != RR_OK || n == 0) return st;
     DeviceState* d = nullptr;
-    if ((st = ensure_device(&d)) != RR_OK) return st;
+    Scratch sc;
+    memset(&sc, 0, sizeof sc);
+    if (noalloc) {
+        int dev = 0;
+        if ((st = current_device(&dev)) != RR_OK) return st;
+        std::lock_guard<std::mutex> lock(g_mu);
+        if ((st = device_info_locked(dev, g_dev[dev])) != RR_OK) return st;
+        uint64_t* base = nullptr;
+        if ((st = scratch_locked(dev, &base)) != RR_OK) return st;
+        d = &g_dev[dev];
+        sc = carve(base);
+    } else if ((st = ensure_device(&d)) != RR_OK) {
+        return st;
+    }
     const uint64_t es = elem_bytes(dt);
     const uint64_t sbytes = (mode == MODE_RS ? (uint64_t)R : 1) * n * es;
     const uint64_t rbytes = (mode == MODE_AG ? (uint64_t)R : 1) * n * es;
@@ -630,9 +729,16 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
         return copy_bytes(recv[0], send[0], n * es, d, s);
     }
     Plan p;
-    if ((st = make_staged_plan(d, R, n, dt, op, nslices, mode, opt, &p)) != RR_OK) return st;
+    if ((st = make_staged_plan(d, R, n, dt, op, nslices, mode, opt, &p,
+                               noalloc ? kScratchSlots : kSlots)) != RR_OK)
+        return st;
     const uint64_t slot_len = round_up(p.chunk_len, 16 / es);
-    if ((st = ensure_fifo(d, (size_t)R * kFifoSlots * slot_len * es)) != RR_OK) return st;
+    const uint64_t fifo_bytes = (uint64_t)R * kFifoSlots * slot_len * es;
+    if (noalloc) {
+        if (fifo_bytes > kScratchFifoBytes) return RR_ERR_UNSUPPORTED;
+    } else if ((st = ensure_fifo(d, (size_t)fifo_bytes)) != RR_OK) {
+        return st;
+    }
 
     StagedArgs a;
     memset(&a, 0, sizeof a);
@@ -640,20 +746,31 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
         a.send[r] = send[r];
         a.recv[r] = recv[r];
     }
-    a.fifo = d->fifo;
     a.slot_len = slot_len;
     a.n = n;
     a.chunk_len = p.chunk_len;
     a.slice_len = p.slice_len;
     a.sub_len = p.sub_len;
-    a.ready = d->sig;
-    a.ready_shadow = d->shadow;
-    a.credit = d->credit;
-    a.credit_shadow = d->credit_shadow;
-    a.xcc_table = d->xcc_table;
-    a.err = d->err;
+    if (noalloc) {
+        a.fifo = sc.fifo;
+        a.ready = sc.ready;
+        a.ready_shadow = sc.ready_shadow;
+        a.credit = sc.credit;
+        a.credit_shadow = sc.credit_shadow;
+        a.xcc_table = sc.xcc_table;
+        a.err = sc.err;
+        a.launch = {sc.launch_gen, sc.launch_exits};
+    } else {
+        a.fifo = d->fifo;
+        a.ready = d->sig;
+        a.ready_shadow = d->shadow;
+        a.credit = d->credit;
+        a.credit_shadow = d->credit_shadow;
+        a.xcc_table = d->xcc_table;
+        a.err = d->err;
+        a.launch = {d->launch_gen, d->launch_exits};
+    }
     a.timeout_ticks = timeout_ticks(d, opt);
-    a.launch = {d->launch_gen, d->launch_exits};
     a.inject = opt ? opt->inject : 0;
     a.R = R;
     a.team = p.team;
@@ -826,6 +943,14 @@ rr_status_t allreduce_ring_staged(const void* const* sendbufs, void* const* recv
                                   size_t count, rr_dtype_t dt, rr_op_t op, int nslices,
                                   const rr_options_t* opt, rr_stream_t stream) {
     return run_staged(sendbufs, recvbufs, R, count, dt, op, nslices, MODE_ALLREDUCE, opt, stream);
+}
+
+rr_status_t allreduce_ring_staged_noalloc(const void* const* sendbufs, void* const* recvbufs,
+                                          int R, size_t count, rr_dtype_t dt, rr_op_t op,
+                                          int nslices, const rr_options_t* opt,
+                                          rr_stream_t stream) {
+    return run_staged(sendbufs, recvbufs, R, count, dt, op, nslices, MODE_ALLREDUCE, opt, stream,
+                      true);
 }
 
 rr_status_t reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int R,
@@ -1059,16 +1184,54 @@ rr_status_t counting_barrier_run_timed(rr_counting_barrier_t* b, int R, int nste
     return run_barrier(b, R, nsteps, ncontexts, expected_per_step, opt, stamps, stream);
 }
 
+// Reads a failure record; if set, copies it out and clears it together with the
+// signals and shadows of the workspace it belongs to.
+static rr_status_t take_record(ErrorRecord* err, uint64_t* sig, uint64_t* shadow, uint64_t* credit,
+                               uint64_t* credit_shadow, int slots, hipStream_t s, ErrorRecord* out,
+                               bool* found) {
+    ErrorRecord e;
+    if (!hip_ok(hipMemcpy(&e, err, sizeof e, hipMemcpyDeviceToHost))) return RR_ERR_HIP;
+    *found = e.flag != 0;
+    if (!*found) return RR_OK;
+    *out = e;
+    rr_status_t st;
+    if ((st = fill(sig, (uint64_t)slots, 0, kSignalStride, s)) != RR_OK) return st;
+    if ((st = fill(shadow, (uint64_t)slots, 0, 1, s)) != RR_OK) return st;
+    if ((st = fill(credit, (uint64_t)slots, 0, kSignalStride, s)) != RR_OK) return st;
+    if ((st = fill(credit_shadow, (uint64_t)slots, 0, 1, s)) != RR_OK) return st;
+    if ((st = fill((uint64_t*)err, sizeof(ErrorRecord) / 8, 0, 1, s)) != RR_OK) return st;
+    return hip_ok(hipStreamSynchronize(s)) ? RR_OK : RR_ERR_HIP;
+}
+
 rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {
-    DeviceState* d = nullptr;
-    rr_status_t st = ensure_device(&d);
+    int dev = 0;
+    rr_status_t st = current_device(&dev);
     if (st != RR_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if (!hip_ok(hipStreamSynchronize(s))) return RR_ERR_HIP;
-    ErrorRecord e;
-    if (!hip_ok(hipMemcpy(&e, d->err, sizeof e, hipMemcpyDeviceToHost))) return RR_ERR_HIP;
+    DeviceState* d = nullptr;
+    uint64_t* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (g_dev[dev].ready) d = &g_dev[dev];
+        base = g_scratch[dev];
+    }
     if (rec) memset(rec, 0, sizeof *rec);
-    if (e.flag == 0) return RR_OK;
+    ErrorRecord e;
+    memset(&e, 0, sizeof e);
+    bool found = false;
+    // the library-owned workspace, if one exists (nothing is allocated here)
+    if (d && (st = take_record(d->err, d->sig, d->shadow, d->credit, d->credit_shadow, kSlots, s,
+                               &e, &found)) != RR_OK)
+        return st;
+    // the static scratch of allreduce_ring_staged_noalloc, if it was used
+    if (!found && base) {
+        const Scratch c = carve(base);
+        if ((st = take_record(c.err, c.ready, c.ready_shadow, c.credit, c.credit_shadow,
+                              kScratchSlots, s, &e, &found)) != RR_OK)
+            return st;
+    }
+    if (!found) return RR_OK;
     if (rec) {
         rec->status = e.status;
         rec->ctx = e.ctx;
@@ -1078,19 +1241,18 @@ rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {
         rec->expected = e.expected;
         rec->observed = e.observed;
     }
-    // clear the record and restore sig == shadow everywhere
-    if ((st = fill(d->sig, kSlots, 0, kSignalStride, s)) != RR_OK) return st;
-    if ((st = fill(d->shadow, kSlots, 0, 1, s)) != RR_OK) return st;
-    if ((st = fill(d->credit, kSlots, 0, kSignalStride, s)) != RR_OK) return st;
-    if ((st = fill(d->credit_shadow, kSlots, 0, 1, s)) != RR_OK) return st;
-    if ((st = fill((uint64_t*)d->err, sizeof(ErrorRecord) / 8, 0, 1, s)) != RR_OK) return st;
-    if (!hip_ok(hipStreamSynchronize(s))) return RR_ERR_HIP;
     return e.status == RR_ERR_TIMEOUT ? RR_ERR_TIMEOUT : RR_ERR_HIP;
 }
 
 rr_status_t rr_init(void) {
     DeviceState* d = nullptr;
-    return ensure_device(&d);
+    rr_status_t st = ensure_device(&d);
+    if (st != RR_OK) return st;
+    int dev = 0;
+    if ((st = current_device(&dev)) != RR_OK) return st;
+    std::lock_guard<std::mutex> lock(g_mu);
+    uint64_t* base = nullptr;
+    return scratch_locked(dev, &base);
 }
 
 rr_status_t rr_workspace_preset(uint64_t value, rr_stream_t stream) {
