@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--team", type=int, default=0)
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--depth", type=int, default=0,
+                    help="lanes each workgroup interleaves (0: the automatic plan)")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="lane groups each workgroup runs one after another (0: automatic)")
     ap.add_argument("--path", default="ring",
                     choices=["ring", "staged", "reduce_scatter", "all_gather", "alltoall"],
                     help="ring: the in-place ring (headline); staged: the out-of-place staged "
@@ -85,6 +89,14 @@ def parse():
                     help="skip the other benchmark workloads (ring path only)")
     ap.add_argument("--r16-sweep", action="store_true",
                     help="R=16 fp32 size sweep, 4 KiB .. 1 GiB per rank: one JSON line per point")
+    ap.add_argument("--host-cost", action="store_true",
+                    help="instead of the AllReduce: host time to enqueue one call (through "
+                         "the C ABI) beside the GPU time of the call, at 8, 16 and 64 ranks "
+                         "and small to mid sizes, with and without the per-call pointer checks")
+    ap.add_argument("--hop-timeline", action="store_true",
+                    help="instead of the headline: one call of the workload with a clock stamp "
+                         "per (lane, rank, hop) (allreduce_ring_timed), summarised as wait "
+                         "and move times per hop and the spread of hop ends across ranks")
     ap.add_argument("--barrier-latency", action="store_true",
                     help="instead of the AllReduce: per-step latency of the counting barrier "
                          "alone for R = 2..64 and 1 or 8 contexts (one JSON line per point)")
@@ -246,8 +258,9 @@ def _plan_for(rr, w, path, opts):
 
 def _opts_for(w, path, args):
     opts = dict(sync=w.sync, team=args.team, block=args.block, flags=args.flags,
-                fused=args.fused)
+                fused=args.fused, depth=args.depth, rounds=args.rounds)
     if path != "ring":
+        opts.pop("depth")
         if w.sync == "barrier":
             opts["sync"] = "auto"  # the staged loop is paced by its credits
         opts.pop("fused")
@@ -364,11 +377,15 @@ def main():
     torch.cuda.set_device(0)
     if args.barrier_latency:
         return barrier_latency(rr, torch, np)
+    if args.host_cost:
+        return host_cost(rr, torch)
     if args.r16_sweep:
         return r16_sweep(rr, torch, np, args.layout)
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
+    if args.hop_timeline:
+        return hop_timeline(rr, torch, np, w, args)
     path = args.path
     opts = _opts_for(w, path, args)
     if path != "ring" and w.count % w.R:
@@ -413,7 +430,7 @@ def main():
             if name == w.name:
                 continue
             wx = workloads_all()[name]
-            ox = _opts_for(wx, "ring", args)
+            ox = dict(sync=wx.sync)  # each with its own automatic plan
             px = _plan_for(rr, wx, "ring", ox)
             rx = Run(rr, torch, np, wx, "ring", ox, args.layout)
             tx, _ = rx.time(args.steps, args.warmup)
@@ -475,6 +492,104 @@ def main():
 def workloads_all():
     import workloads
     return workloads.ALL
+
+
+def hop_timeline(rr, torch, np, w, args):
+    """Where a call's time goes, hop by hop.  After the warm-up calls (inputs
+    restored before each), one call of the workload through allreduce_ring_timed:
+    every (lane, rank, hop) gets the device clock when its workgroup began to wait
+    for the hop's hand-off, when the wait was over and when the hop's arrival was
+    sent.  Printed (one JSON line): the call's span; per hop, the median time
+    moving data and waiting; the share of workgroup time spent waiting; how far
+    apart the ranks of a lane end the same hop (median and 90th percentile over
+    lanes and hops)."""
+    opts = _opts_for(w, "ring", args)
+    opts.pop("fused")
+    rr.init()
+    run = Run(rr, torch, np, w, "ring", opts, args.layout)
+    run.time(max(1, args.steps // 4), args.warmup)
+    run.restore()
+    stamps, khz = rr.allreduce_ring_timed(run.ranks, w.op, w.nslices, **opts)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    st = stamps.cpu().numpy().astype(np.float64) * (1e3 / khz)  # microseconds
+    run.release()
+    t0, t1, t2 = st[..., 0], st[..., 1], st[..., 2]             # (lanes, R, hops)
+    start = t0[:, :, 0].min()
+    wait = (t1 - t0)[:, :, 1:]
+    move = t2 - t1
+    spread = t2.max(axis=1) - t2.min(axis=1)                    # (lanes, hops)
+    busy = (t2 - t0)[:, :, 1:].sum()
+    pct = lambda a, q: round(float(np.percentile(a, q)), 2)
+    p = rr.plan(w.R, w.count, w.dtype, w.nslices, **opts)
+    print(json.dumps({
+        "metric": "hop timeline", "workload": w.name, "sync": p["sync"],
+        "flags": args.flags, "block": p["block"], "team": p["team"], "depth": p["depth"],
+        "rounds": p["rounds"], "lanes": int(st.shape[0]), "hops": int(st.shape[2]),
+        "span_us": round(float(t2.max() - start), 1),
+        "move_us_per_lane_hop": {"p10": pct(move, 10), "p50": pct(move, 50),
+                                 "p90": pct(move, 90)},
+        "wait_us_per_lane_hop": {"p50": pct(wait, 50), "p90": pct(wait, 90),
+                                 "p99": pct(wait, 99)},
+        "wait_share_of_busy_time": round(float(wait.sum() / busy), 4),
+        "hop_end_spread_across_ranks_us": {"p50": pct(spread, 50), "p90": pct(spread, 90)},
+        "clock_khz": khz}), flush=True)
+    return 0
+
+
+def host_cost(rr, torch):
+    """Host microseconds per call: the time the C ABI takes to validate, plan and
+    enqueue one in-place AllReduce (ctypes call included, measured over 200
+    calls issued back to back in batches of 20 with a synchronisation between
+    batches, outside the timed part), beside the GPU time of one call (HIP
+    events, median of 20).  Each point is taken with the per-call pointer checks
+    (the default) and without them (RR_FLAG_NO_POINTER_CHECK); rank buffers are
+    separate tensors.  A call is enqueue-bound when the host time exceeds the
+    GPU time."""
+    import ctypes
+    rr.init()
+    stream = torch.cuda.current_stream()
+    for R in (8, 16, 64):
+        for kib in (4, 64, 1024, 16384):
+            count = kib * 1024 // 4
+            ranks = [torch.zeros(count, device="cuda") for _ in range(R)]
+            ptrs = [t.data_ptr() for t in ranks]
+            p = rr.plan(R, count, "fp32", 4, sync="p2p")
+            row = {"metric": "host cost per call", "R": R, "bytes_per_rank": count * 4,
+                   "nslices": 4, "sync": p["sync"], "grid": p["grid"]}
+            for label, flags in (("checked", 0), ("unchecked", rr.FLAG_NO_POINTER_CHECK)):
+                def call():
+                    st = rr.allreduce_ring_ptrs(ptrs, count, "fp32", "max", 4,
+                                                stream=stream.cuda_stream,
+                                                sync="p2p", flags=flags)
+                    if st != rr.RR_OK:
+                        raise RuntimeError(rr.status_string(st))
+                for _ in range(10):
+                    call()
+                torch.cuda.synchronize()
+                spent, n = 0.0, 0
+                for _ in range(10):
+                    t0 = time.perf_counter()
+                    for _ in range(20):
+                        call()
+                    spent += time.perf_counter() - t0
+                    n += 20
+                    torch.cuda.synchronize()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(20)]
+                for a, e in evs:
+                    a.record(stream)
+                    call()
+                    e.record(stream)
+                torch.cuda.synchronize()
+                rr.check_kernel_error()
+                gpu = sorted(a.elapsed_time(e) for a, e in evs)[10] * 1e3
+                row[f"host_us_{label}"] = round(spent / n * 1e6, 2)
+                row[f"gpu_us_{label}"] = round(gpu, 2)
+            print(json.dumps(row), flush=True)
+            del ranks
+            torch.cuda.empty_cache()
+    return 0
 
 
 def barrier_latency(rr, torch, np):

@@ -155,6 +155,19 @@ typedef enum {
                                          Infinity Cache; see rr_plan_t.stream_loads) */
 #define RR_FLAG_CACHED_LOADS     0x40u /* in-place ring: never mark them (both flags
                                          together: RR_ERR_INVALID) */
+#define RR_FLAG_SHARED_SIGNAL    0x80u /* in-place ring, RR_SYNC_BARRIER: one counting
+                                         signal per lane that all R ranks add 1 to after
+                                         each hop (one atomic per workgroup and hop instead
+                                         of R-1); a waiter expects R arrivals per hop, its
+                                         own included.  Same results */
+#define RR_FLAG_POLL_FAST        0x100u /* in-place ring: sleep about 64 clocks between
+                                          polls of a hand-off signal (the default with
+                                          predecessor hand-offs, and with a barrier whose
+                                          hop moves less than 64 MiB over all ranks) */
+#define RR_FLAG_POLL_MEDIUM      0x200u /* ... about 512 clocks */
+#define RR_FLAG_POLL_SLOW        0x400u /* ... about 4096 clocks (the default with a barrier
+                                          whose hop moves 64 MiB or more).  At most one of
+                                          the three poll flags */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -263,6 +276,28 @@ rr_status_t reduce_scatter_ring_ex(void *const *bufs, int R, size_t count, rr_dt
                                    rr_stream_t stream);
 rr_status_t all_gather_ring_ex(void *const *bufs, int R, size_t count, rr_dtype_t dt,
                                int nslices, const rr_options_t *opt, rr_stream_t stream);
+
+/* allreduce_ring_ex with a clock stamp per hop: the tracing of the ring's own
+   hops (where a hop's time goes: waiting for its hand-off, moving its data; how
+   far apart the ranks finish the same hop), as counting_barrier_run_timed does
+   for the barrier alone.  `stamps` is caller-owned device memory of at least
+   nslices * team * R * 2(R-1) * 3 uint64 words (team as rr_plan_query reports
+   it), 8-byte aligned; `stamp_words` is its length.  For lane l (= slice *
+   team + member), rank r and hop g (1 .. 2(R-1)), the three words at
+   ((l * R + r) * 2(R-1) + g - 1) * 3 receive the device's constant-rate wall
+   clock when the rank's workgroup starts waiting for the hop's hand-off, when
+   the wait is over and the data movement begins, and when the hop's arrival
+   has been sent (for the last hop: when its stores were issued).  The first
+   hop has no wait (its first two words are two clock reads in a row).  *clock_khz receives the clock's
+   rate (host pointer).  Stamps of hops a failed wait skipped stay as they
+   were.  The call allocates nothing beyond allreduce_ring_ex.  Errors: as
+   allreduce_ring_ex, plus RR_ERR_INVALID for a null or misaligned `stamps`, a
+   null `clock_khz`, too few words, or (unless RR_FLAG_NO_POINTER_CHECK) a
+   stamps range outside one device allocation. */
+rr_status_t allreduce_ring_timed(void *const *bufs, int R, size_t count, rr_dtype_t dt,
+                                 rr_op_t op, int nslices, const rr_options_t *opt,
+                                 uint64_t *stamps, size_t stamp_words, uint32_t *clock_khz,
+                                 rr_stream_t stream);
 
 /* ------------------------------------------------- the staged, out-of-place loop */
 

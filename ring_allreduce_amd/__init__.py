@@ -51,6 +51,10 @@ FLAG_FUSED_BOUNDARY = 0x8
 FLAG_AUDIT = 0x10
 FLAG_STREAM_LOADS = 0x20
 FLAG_CACHED_LOADS = 0x40
+FLAG_SHARED_SIGNAL = 0x80
+FLAG_POLL_FAST = 0x100
+FLAG_POLL_MEDIUM = 0x200
+FLAG_POLL_SLOW = 0x400
 
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16",
                  torch.float16: "fp16"}
@@ -104,6 +108,8 @@ _reduce_scatter_ring_ex = _sig("reduce_scatter_ring_ex", _i, ctypes.POINTER(_vp)
                                _i, _OPT, _vp)
 _all_gather_ring_ex = _sig("all_gather_ring_ex", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _OPT, _vp)
 _allreduce_ring = _sig("allreduce_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _vp)
+_allreduce_ring_timed = _sig("allreduce_ring_timed", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i,
+                             _OPT, _vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp)
 _reduce_scatter_ring = _sig("reduce_scatter_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _i, _vp)
 _all_gather_ring = _sig("all_gather_ring", _i, ctypes.POINTER(_vp), _i, _sz, _i, _i, _vp)
 _plan_query = _sig("rr_plan_query", _i, _i, _sz, _i, _i, _i, _OPT, ctypes.POINTER(_Plan))
@@ -138,7 +144,7 @@ _finalize = _sig("rr_finalize", None)
 # Every symbol include/rr.h declares, for the export check.
 EXPORTED = ["allreduce_ring", "reduce_scatter_ring", "all_gather_ring", "allreduce_ring_ex",
             "reduce_scatter_ring_ex", "all_gather_ring_ex", "allreduce_ring_staged",
-            "allreduce_ring_staged_noalloc",
+            "allreduce_ring_staged_noalloc", "allreduce_ring_timed",
             "reduce_scatter", "all_gather", "alltoall", "rr_plan_query",
             "counting_barrier_create", "counting_barrier_destroy", "counting_barrier_reset",
             "counting_barrier_preset", "counting_barrier_read", "counting_barrier_read_peer",
@@ -222,6 +228,27 @@ def allreduce_ring(tensors, op: str = "sum", nslices: int = 1, *, stream=None, *
         else:
             st = _allreduce_ring(ptrs, len(tensors), count, DTYPES[dt], OPS[op], nslices, s)
     _check(st, "allreduce_ring")
+
+
+def allreduce_ring_timed(tensors, op: str = "sum", nslices: int = 1, *, stream=None, **opts):
+    """allreduce_ring with a clock stamp per (lane, rank, hop).  Returns (stamps,
+    clock_khz): stamps is a device tensor of shape (lanes, R, 2(R-1), 3) holding
+    the wall clock when the wait for the hop began, when the hop's data movement
+    began and when its arrival was sent (lanes = nslices * team of the plan)."""
+    ptrs, count, dt = _buffers(tensors)
+    R = len(tensors)
+    p = plan(R, count, dt, nslices, **opts)
+    lanes = nslices * p["team"]
+    stamps = torch.zeros((lanes, R, max(1, 2 * (R - 1)), 3), dtype=torch.int64,
+                         device=tensors[0].device)
+    khz = ctypes.c_uint32(0)
+    with torch.cuda.device(tensors[0].device):
+        o = _options(**opts)
+        st = _allreduce_ring_timed(ptrs, R, count, DTYPES[dt], OPS[op], nslices, ctypes.byref(o),
+                                   stamps.data_ptr(), stamps.numel(), ctypes.byref(khz),
+                                   _stream_handle(stream))
+    _check(st, "allreduce_ring_timed")
+    return stamps, khz.value
 
 
 def reduce_scatter_ring(tensors, op: str = "sum", nslices: int = 1, *, stream=None, **opts) -> None:

@@ -110,13 +110,18 @@ struct DeviceState {
     std::vector<void*> retired;         // receive buffers outgrown, kept until rr_finalize
     uint64_t* launch_gen = nullptr;     // per-launch tag of the XCD table (starts at 1)
     uint64_t* launch_exits = nullptr;   // workgroups of the running launch that have left
+    uint64_t* lane_sig = nullptr;       // barrier with one signal per lane (RR_FLAG_SHARED_SIGNAL)
+    uint64_t* lane_shadow = nullptr;
+    // resident workgroups per CU of each kernel handle, as the occupancy query
+    // answered it (asked once per kernel and device, not once per call)
+    std::vector<std::pair<const void*, int>> occupancy;
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
 struct Plan {
-    int long_nap;
+    int nap;
     int stream_in;
     int fuse;
     int sync;
@@ -171,7 +176,7 @@ static rr_status_t ensure_device(DeviceState** out) {
         // signals (one per cache line), shadows, the XCC table, the error record,
         // the staged loop's credit signals and their shadows, then the launch tag
         // and the exit count (a cache line each)
-        const size_t words = 2 * ((size_t)kSlots * kSignalStride + (size_t)kSlots) +
+        const size_t words = 3 * ((size_t)kSlots * kSignalStride + (size_t)kSlots) +
                              (size_t)kSlots + 16 + 2 * kSignalStride;
         void* p = nullptr;
         if (!hip_ok(hipMalloc(&p, words * sizeof(uint64_t)))) return RR_ERR_NOMEM;
@@ -188,6 +193,8 @@ static rr_status_t ensure_device(DeviceState** out) {
         d.credit_shadow = d.credit + (size_t)kSlots * kSignalStride;
         d.launch_gen = d.credit_shadow + kSlots;
         d.launch_exits = d.launch_gen + kSignalStride;
+        d.lane_sig = d.launch_exits + kSignalStride;
+        d.lane_shadow = d.lane_sig + (size_t)kSlots * kSignalStride;
         const uint64_t first_tag = 1;
         if (!hip_ok(hipMemcpy(d.launch_gen, &first_tag, sizeof first_tag,
                               hipMemcpyHostToDevice))) {
@@ -259,11 +266,20 @@ static rr_status_t check_args(void* const* bufs, int R, size_t count, int dt, in
 }
 
 // Every buffer must lie inside one allocation of the current device, so that no
-// kernel can touch memory outside what the caller handed over.
+// kernel can touch memory outside what the caller handed over.  Buffers inside
+// an allocation already checked in this call (rank buffers carved from one
+// allocation) need no further runtime query.
 static rr_status_t check_extents(void* const* bufs, int R, size_t bytes) {
     int dev = 0;
     if (!hip_ok(hipGetDevice(&dev))) return RR_ERR_HIP;
+    uintptr_t seen_lo[8], seen_hi[8];
+    int nseen = 0;
     for (int r = 0; r < R; ++r) {
+        const uintptr_t b = (uintptr_t)bufs[r];
+        bool inside = false;
+        for (int k = 0; k < nseen && !inside; ++k)
+            inside = b >= seen_lo[k] && b <= seen_hi[k] && bytes <= seen_hi[k] - b;
+        if (inside) continue;
         hipPointerAttribute_t attr;
         if (!hip_ok(hipPointerGetAttributes(&attr, bufs[r]))) {
             (void)hipGetLastError();
@@ -277,16 +293,30 @@ static rr_status_t check_extents(void* const* bufs, int R, size_t bytes) {
             return RR_ERR_INVALID;
         }
         if ((uintptr_t)bufs[r] + bytes > (uintptr_t)base + size) return RR_ERR_INVALID;
+        if (nseen < 8) {
+            seen_lo[nseen] = (uintptr_t)base;
+            seen_hi[nseen] = (uintptr_t)base + size;
+            ++nseen;
+        }
     }
     return RR_OK;
 }
 
+// Workgroups of `kernel` (one instantiation per workgroup size) the device can
+// hold at once.  The answer is fixed per kernel and device, so it is kept.
 static int resident_limit(const DeviceState* d, const void* kernel, int block) {
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        for (const auto& e : d->occupancy)
+            if (e.first == kernel) return e.second * d->cus;
+    }
     int per_cu = 0;
     if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0))) {
         (void)hipGetLastError();
         return 0;
     }
+    std::lock_guard<std::mutex> lock(g_mu);
+    const_cast<DeviceState*>(d)->occupancy.push_back({kernel, per_cu});
     return per_cu * d->cus;
 }
 
@@ -434,22 +464,37 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     // barrier waits poll slowly once one hop moves at least kLongNapBytes over
     // all ranks (about 10 us of traffic, so a later wake-up of up to ~2 us is
     // hidden; smaller buffers are latency-bound and keep the fast poll)
-    p->long_nap = sync == RR_SYNC_BARRIER && 3ull * count * elem_bytes(dt) >= kLongNapBytes;
+    p->nap = sync == RR_SYNC_BARRIER && 3ull * count * elem_bytes(dt) >= kLongNapBytes ? 2 : 0;
+    if (flags & RR_FLAG_POLL_FAST) p->nap = 0;
+    if (flags & RR_FLAG_POLL_MEDIUM) p->nap = 1;
+    if (flags & RR_FLAG_POLL_SLOW) p->nap = 2;
     p->stream_in = (flags & RR_FLAG_STREAM_LOADS) ||
                    (!(flags & RR_FLAG_CACHED_LOADS) && (uint64_t)R * nbytes > kInfinityCacheBytes);
     return RR_OK;
 }
 
+// stamps: optional per-hop clock stamps (allreduce_ring_timed), stamp_words long.
 static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int op, int nslices,
-                            int phase, const rr_options_t* opt, rr_stream_t stream) {
+                            int phase, const rr_options_t* opt, rr_stream_t stream,
+                            uint64_t* stamps = nullptr, size_t stamp_words = 0) {
     rr_status_t st = check_args(bufs, R, count, dt, op, nslices, opt);
     if (st != RR_OK || R == 1 || count == 0) return st;
     DeviceState* d = nullptr;
     if ((st = ensure_device(&d)) != RR_OK) return st;
-    if (!(opt && (opt->flags & RR_FLAG_NO_POINTER_CHECK)))
+    const bool checked = !(opt && (opt->flags & RR_FLAG_NO_POINTER_CHECK));
+    if (checked)
         if ((st = check_extents(bufs, R, count * elem_bytes(dt))) != RR_OK) return st;
     Plan p;
     if ((st = make_plan(d, R, count, dt, op, nslices, phase, opt, &p)) != RR_OK) return st;
+    if (stamps) {
+        // 3 words per (lane, rank, hop of the whole AllReduce)
+        const uint64_t need = (uint64_t)nslices * p.team * R * (2ull * (R - 1)) * 3;
+        if (stamp_words < need) return RR_ERR_INVALID;
+        if (checked) {
+            void* const sb[1] = {stamps};
+            if ((st = check_extents(sb, 1, (size_t)need * sizeof(uint64_t))) != RR_OK) return st;
+        }
+    }
 
     RingArgs a;
     memset(&a, 0, sizeof a);
@@ -470,8 +515,12 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.rounds = p.rounds;
     a.depth = p.depth;
     a.fuse = p.fuse;
-    a.long_nap = p.long_nap;
+    a.nap = p.nap;
     a.stream_in = p.stream_in;
+    a.shared_sig = p.sync == RR_SYNC_BARRIER && (opt && (opt->flags & RR_FLAG_SHARED_SIGNAL)) ? 1 : 0;
+    a.lane_sig = d->lane_sig;
+    a.lane_shadow = d->lane_shadow;
+    a.stamps = stamps;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
     RingKernel k = pick_ring_kernel(dt, op, p.block);
@@ -924,6 +973,17 @@ rr_status_t all_gather_ring_ex(void* const* bufs, int R, size_t count, rr_dtype_
     return run_ring(bufs, R, count, dt, RR_SUM, nslices, 2, opt, stream);
 }
 
+rr_status_t allreduce_ring_timed(void* const* bufs, int R, size_t count, rr_dtype_t dt, rr_op_t op,
+                                 int nslices, const rr_options_t* opt, uint64_t* stamps,
+                                 size_t stamp_words, uint32_t* clock_khz, rr_stream_t stream) {
+    if (!stamps || !clock_khz || (uintptr_t)stamps % 8 != 0) return RR_ERR_INVALID;
+    DeviceState* d = nullptr;
+    rr_status_t st = ensure_device(&d);
+    if (st != RR_OK) return st;
+    *clock_khz = (uint32_t)d->wall_khz;
+    return run_ring(bufs, R, count, dt, op, nslices, 0, opt, stream, stamps, stamp_words);
+}
+
 rr_status_t allreduce_ring(void* const* bufs, int R, size_t count, rr_dtype_t dt, rr_op_t op,
                            int nslices, rr_stream_t stream) {
     return run_ring(bufs, R, count, dt, op, nslices, 0, nullptr, stream);
@@ -1224,6 +1284,11 @@ rr_status_t rr_last_kernel_error(rr_stream_t stream, rr_error_record_t* rec) {
     if (d && (st = take_record(d->err, d->sig, d->shadow, d->credit, d->credit_shadow, kSlots, s,
                                &e, &found)) != RR_OK)
         return st;
+    if (d && found) {
+        if ((st = fill(d->lane_sig, kSlots, 0, kSignalStride, s)) != RR_OK) return st;
+        if ((st = fill(d->lane_shadow, kSlots, 0, 1, s)) != RR_OK) return st;
+        if (!hip_ok(hipStreamSynchronize(s))) return RR_ERR_HIP;
+    }
     // the static scratch of allreduce_ring_staged_noalloc, if it was used
     if (!found && base) {
         const Scratch c = carve(base);
@@ -1263,6 +1328,8 @@ rr_status_t rr_workspace_preset(uint64_t value, rr_stream_t stream) {
     if ((st = fill(d->sig, kSlots, value, kSignalStride, s)) != RR_OK) return st;
     if ((st = fill(d->shadow, kSlots, value, 1, s)) != RR_OK) return st;
     if ((st = fill(d->credit, kSlots, value, kSignalStride, s)) != RR_OK) return st;
+    if ((st = fill(d->lane_sig, kSlots, value, kSignalStride, s)) != RR_OK) return st;
+    if ((st = fill(d->lane_shadow, kSlots, value, 1, s)) != RR_OK) return st;
     return fill(d->credit_shadow, kSlots, value, 1, s);
 }
 

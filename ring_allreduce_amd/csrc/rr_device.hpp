@@ -182,20 +182,22 @@ struct WaitResult {
 // Called by one lane.  Returns once rolling_le(target, *sig); gives up after
 // `timeout_ticks` of the constant-rate wall clock, or as soon as another
 // waiter on the device has given up (err->flag set).
-// long_nap: poll about every 4096 clocks instead of every 64.  A counting
-// barrier's signal takes R-1 atomic adds per step; frequent polls of the same
-// line slow them and the data traffic around them, which costs more than the
-// later wake-up once a hop moves enough data (the R=64 ring: +2%).
+// nap: how long to sleep between polls -- 0: 64 clocks, 1: 512, 2: 4096.  A
+// counting barrier's signal takes R-1 atomic adds per step; frequent polls of
+// the same line slow them and the data traffic around them, which costs more
+// than the later wake-up once a hop moves enough data (the R=64 ring: +2%).
 __device__ __forceinline__ WaitResult sig_wait(const uint64_t* sig, uint64_t target,
                                                const ErrorRecord* err, uint64_t timeout_ticks,
-                                               bool long_nap = false) {
+                                               int nap = 0) {
     uint64_t v = sig_read(sig);
     if (rolling_le(target, v)) return {WAIT_OK, v};
     const uint64_t start = wall_clock64();
     uint32_t spins = 0;
     for (;;) {
-        if (long_nap)
+        if (nap >= 2)
             __builtin_amdgcn_s_sleep(64);
+        else if (nap == 1)
+            __builtin_amdgcn_s_sleep(8);
         else
             __builtin_amdgcn_s_sleep(1);
         v = sig_read(sig);

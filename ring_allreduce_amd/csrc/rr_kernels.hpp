@@ -53,8 +53,14 @@ struct RingArgs {
     int32_t cols;        // workgroups per rank = grid / R
     int32_t rounds;      // lane groups each workgroup runs one after another
     int32_t depth;       // lanes each workgroup interleaves hop by hop (1..kMaxDepth)
-    int32_t long_nap;    // barrier waits poll slowly (a hop moves enough data to hide it)
+    int32_t nap;         // sleep between polls of a wait: 0 short, 1 medium, 2 long
     int32_t stream_in;   // loads of the predecessor's buffer are non-temporal
+    int32_t shared_sig;  // barrier: one signal per lane that all R ranks add to
+    int32_t pad;
+    uint64_t* lane_sig;    // shared_sig: signal of lane l at lane_sig[l * kSignalStride]
+    uint64_t* lane_shadow; // shared_sig: the lane's shadow (every rank's waiter tracks it)
+    uint64_t* stamps;      // optional: wall clock per (lane, rank, hop): wait begins, hop
+                           // begins, hop ends (after its arrival); 3 words each
 };
 
 // The staged loop: receive slots per (lane, rank), threads per workgroup.

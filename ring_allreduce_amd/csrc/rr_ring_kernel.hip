@@ -155,7 +155,12 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
     // ReduceScatter, the finished chunk one AllGather hop later).
     bool local = false;
     bool decided = false;
-    const uint64_t arrivals = a.sync == SYNC_BARRIER ? (uint64_t)(R - 1) : 1;
+    // Arrivals a waiter expects per hop: its predecessor's (P2P); the R-1 other
+    // ranks' (barrier, a signal per waiter); all R ranks' (barrier, one signal
+    // per lane that every rank of the lane adds to, its own arrival included).
+    const bool shared = a.sync == SYNC_BARRIER && a.shared_sig != 0;
+    const uint64_t arrivals =
+        a.sync == SYNC_BARRIER ? (uint64_t)(shared ? R : R - 1) : 1;
     __shared__ int s_stop_lane[kMaxDepth];
 
     // Lane groups one after another: only cols * depth lanes are in flight at
@@ -177,7 +182,8 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
             off_hi[p] = umin(off_lo[p] + a.sub_len,
                              umin((uint64_t)(j + 1) * a.slice_len, a.chunk_len));
             shadow[p] = 0;
-            if (p < a.depth && synced && threadIdx.x == 0) shadow[p] = a.shadow[lane[p] * R + r];
+            if (p < a.depth && synced && threadIdx.x == 0)
+                shadow[p] = shared ? a.lane_shadow[lane[p]] : a.shadow[lane[p] * R + r];
         }
 
         for (int g = a.g_first; g <= a.g_last; ++g) {
@@ -186,15 +192,19 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
                 if (p >= a.depth) break;
                 const int my_slot = lane[p] * R + r;
                 const bool injected = r == 0 && lane[p] == 0;
+                uint64_t t_wait = 0, t_hop = 0;
+                if (a.stamps && threadIdx.x == 0) t_wait = wall_clock64();
                 if (g > a.g_first) {
                     if (threadIdx.x == 0) {
                         uint64_t target = shadow[p] + arrivals;
                         if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected &&
                             g == a.g_first + 1)
                             target += 1;
-                        const WaitResult res = sig_wait(&a.sig[(uint64_t)my_slot * kSignalStride],
-                                                        target, a.err, a.timeout_ticks,
-                                                        a.long_nap != 0);
+                        const uint64_t* wsig =
+                            shared ? &a.lane_sig[(uint64_t)lane[p] * kSignalStride]
+                                   : &a.sig[(uint64_t)my_slot * kSignalStride];
+                        const WaitResult res =
+                            sig_wait(wsig, target, a.err, a.timeout_ticks, a.nap);
                         if (res.status == WAIT_TIMEOUT)
                             record_timeout(a.err, lane[p], r, g, target, res.observed);
                         shadow[p] = target;
@@ -204,6 +214,7 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
                     __syncthreads();
                     if (s_stop_lane[p]) return;
                 }
+                if (a.stamps && threadIdx.x == 0) t_hop = wall_clock64();
 
                 int c;
                 bool reduce;
@@ -247,7 +258,10 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
                     const bool drop =
                         (a.inject & RR_INJECT_DROP_ARRIVAL) && injected && g == a.g_first;
                     if (!drop) {
-                        if (a.sync == SYNC_BARRIER) {
+                        if (shared) {
+                            if (threadIdx.x == 0)
+                                sig_add(&a.lane_sig[(uint64_t)lane[p] * kSignalStride], 1);
+                        } else if (a.sync == SYNC_BARRIER) {
                             if ((int)threadIdx.x < R - 1) {
                                 const int q = wrap(r + 1 + (int)threadIdx.x, R);
                                 sig_add(&a.sig[(uint64_t)(lane[p] * R + q) * kSignalStride], 1);
@@ -257,12 +271,24 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
                         }
                     }
                 }
+                if (a.stamps && threadIdx.x == 0) {
+                    uint64_t* st = a.stamps +
+                                   ((uint64_t)my_slot * (2 * (R - 1)) + (uint64_t)(g - 1)) * 3;
+                    st[0] = t_wait;
+                    st[1] = t_hop;
+                    st[2] = wall_clock64();
+                }
             }
         }
         if (synced && threadIdx.x == 0) {
 #pragma unroll
             for (int p = 0; p < kMaxDepth; ++p)
-                if (p < a.depth) a.shadow[lane[p] * R + r] = shadow[p];  // sig == shadow again
+                if (p < a.depth) {  // signal == shadow again
+                    if (shared)
+                        a.lane_shadow[lane[p]] = shadow[p];  // every rank stores the same value
+                    else
+                        a.shadow[lane[p] * R + r] = shadow[p];
+                }
         }
     }
 }

@@ -75,6 +75,23 @@ def test_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"R={R} count={count}")
 
 
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("bf16", "max"),
+                                      ("bf16", "sum")])
+@pytest.mark.parametrize("R,count,nslices,team", SMALL)
+@pytest.mark.parametrize("depth", [1, 2])
+def test_shared_lane_signal_small_ragged(rr, dtype, op, R, count, nslices, team, depth):
+    """A barrier per hop through one counting signal per lane that all R ranks add
+    to (a waiter expects R arrivals): the same bits as the oracle."""
+    if (nslices * team) % depth:
+        pytest.skip("depth must divide the lanes")
+    log(f"case shared signal {dtype} {op} R={R} count={count} ns={nslices} team={team} "
+        f"depth={depth}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], R * 37 + count % 89)
+    got = run_case(rr, x, dtype, op, nslices, sync="barrier", team=team, depth=depth,
+                   flags=rr.FLAG_SHARED_SIGNAL)
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"shared R={R} count={count}")
+
+
 # ------------------------------------- load policy (non-temporal incoming loads)
 
 @pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("bf16", "max")])
@@ -405,10 +422,10 @@ def test_rolling_counters_near_wrap(rr):
     x = workloads.generate(R, count, "fp32", "uniform_pm1", 9)
     expect = oracle_expect(x, "sum")
     rr.workspace_preset((1 << 64) - 3)
-    for sync in ("p2p", "barrier"):
-        log(f"case wrap sync={sync}")
-        got = run_case(rr, x, "fp32", "sum", 4, sync=sync)
-        assert_matches_oracle(got, expect, "fp32", f"wrap {sync}")
+    for sync, flags in (("p2p", 0), ("barrier", 0), ("barrier", rr.FLAG_SHARED_SIGNAL)):
+        log(f"case wrap sync={sync} flags={flags}")
+        got = run_case(rr, x, "fp32", "sum", 4, sync=sync, flags=flags)
+        assert_matches_oracle(got, expect, "fp32", f"wrap {sync} {flags}")
     rr.workspace_preset(0)
     torch.cuda.synchronize()
 
@@ -557,6 +574,13 @@ def test_full_fused_boundary(rr, w):
     _full_size(rr, w, 5000, dict(fused=True))
 
 
+@pytest.mark.parametrize("w", [workloads.R64_FP32_32MIB, workloads.r16_sweep(8, "sum", 16)],
+                         ids=lambda w: w.name)
+def test_full_shared_lane_signal(rr, w):
+    """The barrier workloads with one shared counting signal per lane."""
+    _full_size(rr, w.with_(sync="barrier"), 4000, dict(flags=rr.FLAG_SHARED_SIGNAL))
+
+
 def test_full_cached_loads(rr):
     """The default workload with the hint forced off (its default is on)."""
     _full_size(rr, workloads.R8_FP32_64MIB, 5000, dict(loads="cached"))
@@ -640,3 +664,37 @@ def test_pieces_longer_than_one_descriptor(rr):
     oracle.allreduce(x, "sum")
     assert_full_matches(send.ranks, x, "fp32", "ring, 2 GiB per rank")
     assert_full_matches(recv, x, "fp32", "staged, 2 GiB per rank")
+
+
+@pytest.mark.parametrize("sync,flags", [("p2p", 0), ("barrier", 0), ("barrier", "shared")])
+def test_hop_stamps(rr, sync, flags):
+    """allreduce_ring_timed: the same bits as the oracle, and stamps that respect
+    the hand-off order.  Per (lane, rank, hop): wait begins <= hop begins <= hop
+    ends.  A hop begins only after the hop it waits for has begun: the
+    predecessor's previous hop (P2P), every rank's previous hop (barrier)."""
+    R, count, ns = 8, 8 * 4096 * 3 + 5, 3
+    f = rr.FLAG_SHARED_SIGNAL if flags == "shared" else 0
+    log(f"case hop stamps sync={sync} flags={f}")
+    x = workloads.generate(R, count, "fp32", "uniform_pm1", 61)
+    slabs = to_slabs(rr, x, "fp32")
+    stamps, khz = rr.allreduce_ring_timed(slabs.ranks, "sum", ns, sync=sync, flags=f)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert khz > 0
+    assert guards_intact(slabs, "fp32", count)
+    assert_matches_oracle([to_host(t, "fp32") for t in slabs.ranks], oracle_expect(x, "sum"),
+                          "fp32", "timed call")
+    st = stamps.cpu().numpy().astype(np.int64)            # (lanes, R, hops, 3)
+    p = rr.plan(R, count, "fp32", ns, sync=sync)
+    assert st.shape == (ns * p["team"], R, 2 * (R - 1), 3)
+    assert (st > 0).all()
+    assert (st[..., 0] <= st[..., 1]).all() and (st[..., 1] <= st[..., 2]).all()
+    # the first hop does not wait: its first two stamps are two clock reads in a row
+    assert ((st[:, :, 0, 1] - st[:, :, 0, 0]) * 1e6 / (khz * 1e3) < 5.0).all()
+    begin = st[..., 1]
+    for g in range(1, 2 * (R - 1)):
+        if sync == "p2p":
+            prev = np.roll(begin[:, :, g - 1], 1, axis=1)  # rank r-1's previous hop
+        else:
+            prev = begin[:, :, g - 1].max(axis=1, keepdims=True)
+        assert (begin[:, :, g] >= prev).all(), g
