@@ -597,6 +597,8 @@ def barrier_latency(rr, torch, np):
     workgroup per (context, waiter); per step each waiter arrives and waits.
       barrier   counting signal: adds 1 to each other waiter's one signal, waits
                 for its own to advance by R-1
+      shared    one signal per context: every waiter adds 1 to it and waits for
+                it to advance by R (the ring's default barrier layout)
       per_peer  per-peer slots: adds 1 to its own slot in each other waiter's
                 row, waits for each of the R-1 slots of its row to advance by 1
       p2p       adds 1 to its successor's signal, waits for 1
@@ -625,14 +627,14 @@ def barrier_latency(rr, torch, np):
         return best
 
     steps = 2000
-    for mode in ("barrier", "per_peer", "p2p"):
+    for mode in ("barrier", "shared", "per_peer", "p2p"):
         for nctx in (1, 8):
             for R in (2, 4, 8, 16, 32, 64):
                 b.run(R, 100, nctx, mode=mode)  # warm
                 t0 = timed(R, 0, nctx, mode)
                 t1 = timed(R, steps, nctx, mode)
                 us = (t1 - t0) * 1e3 / steps
-                per_waiter = 1 if mode == "p2p" else R - 1
+                per_waiter = 1 if mode in ("p2p", "shared") else R - 1
                 # in-kernel view: each waiter's step times from the device clock, and
                 # how far apart the waiters of a context leave the same step
                 st, khz = b.run_timed(R, steps, nctx, mode=mode)

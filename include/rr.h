@@ -109,7 +109,10 @@ typedef enum {
                             rank's workgroup in the same lane only (1 arrival per hop) */
     RR_SYNC_BARRIER = 2, /* persistent kernel; every hop ends with a counting barrier
                             over all R ranks of the lane: each workgroup adds 1 to
-                            every other rank's signal, a waiter expects R-1 */
+                            the lane's one shared signal and waits until it has
+                            advanced by R (the R-1 other ranks and itself); with
+                            RR_FLAG_WAITER_SIGNAL each workgroup adds 1 to every
+                            other rank's own signal, a waiter expects R-1 */
     RR_SYNC_LAUNCH = 3,  /* one kernel launch per hop; stream order is the barrier */
     RR_SYNC_PER_PEER = 4 /* counting_barrier_run only: one slot per (waiter, peer);
                             each peer adds 1 to its own slot and a waiter waits for
@@ -155,11 +158,16 @@ typedef enum {
                                          Infinity Cache; see rr_plan_t.stream_loads) */
 #define RR_FLAG_CACHED_LOADS     0x40u /* in-place ring: never mark them (both flags
                                          together: RR_ERR_INVALID) */
-#define RR_FLAG_SHARED_SIGNAL    0x80u /* in-place ring, RR_SYNC_BARRIER: one counting
-                                         signal per lane that all R ranks add 1 to after
-                                         each hop (one atomic per workgroup and hop instead
-                                         of R-1); a waiter expects R arrivals per hop, its
-                                         own included.  Same results */
+#define RR_FLAG_SHARED_SIGNAL    0x80u /* counting_barrier_run, RR_SYNC_BARRIER: one
+                                         signal per context that every waiter adds 1 to
+                                         and polls (pass expected_per_step = R); the in-
+                                         place ring's barrier does this by default */
+#define RR_FLAG_WAITER_SIGNAL    0x800u /* in-place ring, RR_SYNC_BARRIER: one signal per
+                                         (lane, rank) instead of one per lane; after each
+                                         hop a workgroup adds 1 to the R-1 other ranks'
+                                         signals (R-1 atomics instead of 1) and waits for
+                                         R-1 on its own.  Same results.  Not together with
+                                         RR_FLAG_SHARED_SIGNAL */
 #define RR_FLAG_POLL_FAST        0x100u /* in-place ring: sleep about 64 clocks between
                                           polls of a hand-off signal (the default with
                                           predecessor hand-offs, and with a barrier whose
@@ -167,7 +175,7 @@ typedef enum {
 #define RR_FLAG_POLL_MEDIUM      0x200u /* ... about 512 clocks */
 #define RR_FLAG_POLL_SLOW        0x400u /* ... about 4096 clocks (the default with a barrier
                                           whose hop moves 64 MiB or more).  At most one of
-                                          the three poll flags */
+                                          the three poll flags (else RR_ERR_INVALID) */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -393,7 +401,9 @@ rr_status_t rr_plan_query(int R, size_t count, rr_dtype_t dt, int nslices, int p
    "Fix": one signal per waiter whatever the team size), plus, for comparison,
    the per-peer layout that pull request replaced: a row of nwaiters slots and
    shadows per waiter.  Caller-owned; lives in device memory of the current
-   device: about ncontexts * nwaiters * (144 + 16 * round_up(nwaiters, 16)) bytes. */
+   device: about ncontexts * nwaiters * (144 + 16 * round_up(nwaiters, 16)) bytes,
+   plus one signal and shadow per context for the shared layout
+   (RR_FLAG_SHARED_SIGNAL). */
 typedef struct rr_counting_barrier rr_counting_barrier_t;
 
 /* Errors: RR_ERR_INVALID (nwaiters outside 1..64, ncontexts outside 1..1024,
@@ -414,7 +424,9 @@ rr_status_t counting_barrier_preset(rr_counting_barrier_t *b, uint64_t value, rr
 /* Reads one waiter's signal and shadow, synchronously (waits for the device):
    the signal's current value, as the read method of the 2kiu.com article on NCCL
    GIN (section "Signal methods") returns it, and the shadow the waiter keeps.
-   Errors: RR_ERR_INVALID (b NULL, ctx or waiter out of range), RR_ERR_HIP. */
+   waiter -1 reads the context's shared signal (RR_FLAG_SHARED_SIGNAL) and its
+   shadow.  Errors: RR_ERR_INVALID (b NULL, ctx or waiter out of range),
+   RR_ERR_HIP. */
 rr_status_t counting_barrier_read(rr_counting_barrier_t *b, int ctx, int waiter, uint64_t *value,
                                   uint64_t *shadow);
 
@@ -437,11 +449,13 @@ rr_status_t counting_barrier_early_passes(rr_counting_barrier_t *b, int ctx, int
    waiter's one signal, the waiter advances its shadow by the expected arrivals
    and polls that signal), or, for comparison, the layouts below.  Per step a
    waiter arrives (opt->sync RR_SYNC_BARRIER or AUTO: adds 1 to every other
-   waiter's signal in its context; RR_SYNC_P2P: adds 1 to its successor's;
+   waiter's signal in its context, or with RR_FLAG_SHARED_SIGNAL to the
+   context's one signal; RR_SYNC_P2P: adds 1 to its successor's;
    RR_SYNC_PER_PEER: adds 1 to its own slot in every other waiter's row) and
    then advances its shadow by `expected_per_step` and waits for its own signal
-   (per peer: advances every slot's shadow by it and waits for every slot).
-   The right expectation is R-1 (barrier) or 1 (p2p, per peer); a larger one
+   (shared: the context's; per peer: advances every slot's shadow by it and
+   waits for every slot).  The right expectation is R-1 (barrier), R (shared)
+   or 1 (p2p, per peer); a larger one
    times out (RR_ERR_TIMEOUT from rr_last_kernel_error, with the missing count;
    per peer also with the missing peer).  With nsteps == 0 it launches the same
    kernel doing nothing, to time the launch.

@@ -52,6 +52,7 @@ FLAG_AUDIT = 0x10
 FLAG_STREAM_LOADS = 0x20
 FLAG_CACHED_LOADS = 0x40
 FLAG_SHARED_SIGNAL = 0x80
+FLAG_WAITER_SIGNAL = 0x800
 FLAG_POLL_FAST = 0x100
 FLAG_POLL_MEDIUM = 0x200
 FLAG_POLL_SLOW = 0x400
@@ -471,10 +472,22 @@ class CountingBarrier:
         self.nwaiters = nwaiters
         self.ncontexts = ncontexts
 
-    def run(self, R: int, nsteps: int, ncontexts: int = 1, expected: int | None = None,
-            mode: str = "barrier", stream=None, **opts) -> None:
+    @staticmethod
+    def _mode(R, mode, expected, opts):
+        """mode: barrier (a signal per waiter), shared (one per context), per_peer, p2p."""
+        if mode == "shared":
+            opts = dict(opts)
+            opts["flags"] = opts.get("flags", 0) | FLAG_SHARED_SIGNAL
+            mode = "barrier"
+            if expected is None:
+                expected = R
         if expected is None:
             expected = R - 1 if mode == "barrier" else 1  # p2p and per_peer: 1 per slot
+        return mode, expected, opts
+
+    def run(self, R: int, nsteps: int, ncontexts: int = 1, expected: int | None = None,
+            mode: str = "barrier", stream=None, **opts) -> None:
+        mode, expected, opts = self._mode(R, mode, expected, opts)
         o = _options(sync=mode, **opts)
         _check(_cb_run(self._h, R, nsteps, ncontexts, expected, ctypes.byref(o),
                        _stream_handle(stream)), "counting_barrier_run")
@@ -485,8 +498,7 @@ class CountingBarrier:
         is a uint64 tensor on the GPU of shape (ncontexts, R, nsteps + 1), the
         device's constant-rate clock before each waiter's first step and when each
         of its steps' waits was over (valid once the stream has synchronised)."""
-        if expected is None:
-            expected = R - 1 if mode == "barrier" else 1
+        mode, expected, opts = self._mode(R, mode, expected, opts)
         dev = torch.device("cuda", torch.cuda.current_device())
         stamps = torch.zeros((ncontexts, R, nsteps + 1), dtype=torch.int64, device=dev)
         khz = ctypes.c_uint32()

@@ -110,7 +110,7 @@ struct DeviceState {
     std::vector<void*> retired;         // receive buffers outgrown, kept until rr_finalize
     uint64_t* launch_gen = nullptr;     // per-launch tag of the XCD table (starts at 1)
     uint64_t* launch_exits = nullptr;   // workgroups of the running launch that have left
-    uint64_t* lane_sig = nullptr;       // barrier with one signal per lane (RR_FLAG_SHARED_SIGNAL)
+    uint64_t* lane_sig = nullptr;       // barrier: one signal per lane (unless RR_FLAG_WAITER_SIGNAL)
     uint64_t* lane_shadow = nullptr;
     // resident workgroups per CU of each kernel handle, as the occupancy query
     // answered it (asked once per kernel and device, not once per call)
@@ -231,6 +231,12 @@ static rr_status_t check_shape(int R, uint64_t count, int phase, const rr_option
         return RR_ERR_INVALID;
     }
     if (!opt) return RR_OK;
+    // flags that exclude each other
+    if ((opt->flags & RR_FLAG_SHARED_SIGNAL) && (opt->flags & RR_FLAG_WAITER_SIGNAL))
+        return RR_ERR_INVALID;
+    const uint32_t polls =
+        opt->flags & (RR_FLAG_POLL_FAST | RR_FLAG_POLL_MEDIUM | RR_FLAG_POLL_SLOW);
+    if (polls & (polls - 1)) return RR_ERR_INVALID;
     const int max_sync = phase == 6 ? RR_SYNC_P2P : RR_SYNC_LAUNCH;
     if (opt->sync < RR_SYNC_AUTO || opt->sync > max_sync) return RR_ERR_INVALID;
     if (opt->team < 0 || opt->team > (phase == 6 ? 65536 : 4096)) return RR_ERR_INVALID;
@@ -517,7 +523,9 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.fuse = p.fuse;
     a.nap = p.nap;
     a.stream_in = p.stream_in;
-    a.shared_sig = p.sync == RR_SYNC_BARRIER && (opt && (opt->flags & RR_FLAG_SHARED_SIGNAL)) ? 1 : 0;
+    // a barrier per hop: one signal per lane shared by all R ranks, unless the
+    // caller asks for one signal per waiter
+    a.shared_sig = p.sync == RR_SYNC_BARRIER && !(opt && (opt->flags & RR_FLAG_WAITER_SIGNAL)) ? 1 : 0;
     a.lane_sig = d->lane_sig;
     a.lane_shadow = d->lane_shadow;
     a.stamps = stamps;
@@ -952,6 +960,8 @@ struct rr_counting_barrier {
     uint64_t* pp_sig;    // per-peer slots, one row per (context, waiter)
     uint64_t* pp_shadow;
     uint64_t* early;     // early passes seen by audited runs
+    uint64_t* ctx_sig;   // shared layout: one signal per context, stride kSignalStride
+    uint64_t* ctx_shadow;
 };
 
 extern "C" {
@@ -1075,7 +1085,8 @@ rr_status_t counting_barrier_create(int nwaiters, int ncontexts, rr_counting_bar
     if (!hip_ok(hipGetDevice(&dev))) return RR_ERR_HIP;
     const size_t slots = (size_t)nwaiters * ncontexts;
     const int pp_row = (int)round_up((uint64_t)nwaiters, 16);
-    const size_t words = slots * kSignalStride + slots + 2 * slots * pp_row + slots;
+    const size_t words = slots * kSignalStride + slots + 2 * slots * pp_row + slots +
+                         (size_t)ncontexts * kSignalStride + (size_t)ncontexts;
     void* p = nullptr;
     if (!hip_ok(hipMalloc(&p, words * sizeof(uint64_t)))) return RR_ERR_NOMEM;
     if (!hip_ok(hipMemset(p, 0, words * sizeof(uint64_t)))) {
@@ -1097,6 +1108,8 @@ rr_status_t counting_barrier_create(int nwaiters, int ncontexts, rr_counting_bar
     b->pp_sig = b->shadow + slots;
     b->pp_shadow = b->pp_sig + slots * pp_row;
     b->early = b->pp_shadow + slots * pp_row;
+    b->ctx_sig = b->early + slots;
+    b->ctx_shadow = b->ctx_sig + (size_t)ncontexts * kSignalStride;
     *out = b;
     return RR_OK;
 }
@@ -1118,6 +1131,8 @@ rr_status_t counting_barrier_preset(rr_counting_barrier_t* b, uint64_t value, rr
     if (st == RR_OK) st = fill(b->shadow, slots, value, 1, s);
     if (st == RR_OK) st = fill(b->pp_sig, 2 * slots * b->pp_row, value, 1, s);  // with shadows
     if (st == RR_OK) st = fill(b->early, slots, 0, 1, s);
+    if (st == RR_OK) st = fill(b->ctx_sig, (uint64_t)b->ncontexts, value, kSignalStride, s);
+    if (st == RR_OK) st = fill(b->ctx_shadow, (uint64_t)b->ncontexts, value, 1, s);
     return st;
 }
 
@@ -1127,15 +1142,17 @@ rr_status_t counting_barrier_reset(rr_counting_barrier_t* b, rr_stream_t stream)
 
 rr_status_t counting_barrier_read(rr_counting_barrier_t* b, int ctx, int waiter, uint64_t* value,
                                   uint64_t* shadow) {
-    if (!b || ctx < 0 || ctx >= b->ncontexts || waiter < 0 || waiter >= b->nwaiters)
+    if (!b || ctx < 0 || ctx >= b->ncontexts || waiter < -1 || waiter >= b->nwaiters)
         return RR_ERR_INVALID;
     if (!hip_ok(hipDeviceSynchronize())) return RR_ERR_HIP;
     const size_t slot = (size_t)ctx * b->nwaiters + waiter;
+    // waiter -1: the context's shared signal and its shadow
+    const uint64_t* vp = waiter < 0 ? b->ctx_sig + (size_t)ctx * kSignalStride
+                                    : b->sig + slot * kSignalStride;
+    const uint64_t* sp = waiter < 0 ? b->ctx_shadow + ctx : b->shadow + slot;
     uint64_t v = 0, sh = 0;
-    if (!hip_ok(hipMemcpy(&v, b->sig + slot * kSignalStride, sizeof v, hipMemcpyDeviceToHost)))
-        return RR_ERR_HIP;
-    if (!hip_ok(hipMemcpy(&sh, b->shadow + slot, sizeof sh, hipMemcpyDeviceToHost)))
-        return RR_ERR_HIP;
+    if (!hip_ok(hipMemcpy(&v, vp, sizeof v, hipMemcpyDeviceToHost))) return RR_ERR_HIP;
+    if (!hip_ok(hipMemcpy(&sh, sp, sizeof sh, hipMemcpyDeviceToHost))) return RR_ERR_HIP;
     if (value) *value = v;
     if (shadow) *shadow = sh;
     return RR_OK;
@@ -1202,6 +1219,9 @@ static rr_status_t run_barrier(rr_counting_barrier_t* b, int R, int nsteps, int 
                   : opt->sync == RR_SYNC_PER_PEER ? SYNC_PER_PEER : SYNC_BARRIER;
     a.inject = opt ? opt->inject : 0;
     a.audit = opt && (opt->flags & RR_FLAG_AUDIT) ? 1 : 0;
+    a.shared = opt && (opt->flags & RR_FLAG_SHARED_SIGNAL) ? 1 : 0;
+    a.ctx_sig = b->ctx_sig;
+    a.ctx_shadow = b->ctx_shadow;
     a.stamps = stamps;
     void* args[] = {&a};
     hipStream_t s = (hipStream_t)stream;

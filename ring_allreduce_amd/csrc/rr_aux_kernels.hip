@@ -145,7 +145,9 @@ __device__ PeerWait peer_wait(const uint64_t* slot, bool active, uint64_t target
 // Arrivals per step:
 //   P2P       one add to the successor's counting signal
 //   BARRIER   one add to each other waiter's counting signal; the waiter
-//             expects R-1 on its own (the DeepEP pull request's counting barrier)
+//             expects R-1 on its own (the DeepEP pull request's counting barrier);
+//             shared: one add to the context's one signal, which every waiter
+//             of the context polls, expecting R (its own arrival included)
 //   PER_PEER  one add to this waiter's slot in each other waiter's row; the
 //             waiter expects every slot of its row to advance (the per-peer
 //             layout the pull request replaced)
@@ -154,12 +156,15 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
     const int r = pl.rank, ctx = pl.col;
     if (ctx >= a.nctx || a.nsteps <= 0) return;
     const int slot = ctx * a.stride + r;
+    const bool shared = a.shared && a.mode == SYNC_BARRIER;
+    uint64_t* const wait_sig =
+        shared ? &a.ctx_sig[(uint64_t)ctx * kSignalStride] : &a.sig[(uint64_t)slot * kSignalStride];
     const uint32_t my_xcc = xcc_id() & 0xFu;
     __shared__ int s_stop;
     uint64_t shadow = 0;
     if (threadIdx.x == 0) {
         s_stop = sig_read(&a.err->flag) != 0;
-        shadow = a.shadow[slot];
+        shadow = shared ? a.ctx_shadow[ctx] : a.shadow[slot];
         publish_xcc(a.xcc_table, generation, my_xcc);
     }
     __syncthreads();
@@ -176,7 +181,7 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
     const bool peer_lane = lane < a.R - 1;
     const int q = wrap(r + 1 + lane, a.R);
     const bool per_peer = a.mode == SYNC_PER_PEER;
-    const bool audit = a.audit && a.mode == SYNC_BARRIER;
+    const bool audit = a.audit && a.mode == SYNC_BARRIER && !shared;
     const bool use_pp = per_peer || audit;
     // my slot in q's row (where I arrive) and q's slot in my row (what I watch)
     uint64_t* const out_pp = a.pp_sig + (uint64_t)(ctx * a.stride + q) * a.pp_row + r;
@@ -188,7 +193,8 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
     // step-2 arrivals at waiter 1 until it has passed step 2 (with one step,
     // until the end).  Its step-2 arrival must be held too: otherwise it stands
     // in for its own late step-1 arrival, which both layouts allow.
-    const bool defer = (a.inject & RR_INJECT_DEFER_ARRIVAL) && injected && peer_lane && q == 1;
+    const bool defer =
+        (a.inject & RR_INJECT_DEFER_ARRIVAL) && injected && peer_lane && q == 1 && !shared;
     // optional timestamps: the constant-rate wall clock before the first step and
     // when each step's wait is over (lane 0 of the waiter's wave)
     uint64_t* const stamps =
@@ -214,6 +220,8 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
         if (!drop) {
             if (a.mode == SYNC_P2P) {
                 if (lane == 0) sig_add(&a.sig[(uint64_t)(ctx * a.stride + q) * kSignalStride], 1);
+            } else if (shared) {
+                if (lane == 0) sig_add(wait_sig, 1);
             } else if (peer_lane && !(defer && step <= 2)) {
                 arrive();
             }
@@ -234,8 +242,7 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
             if (lane == 0) {
                 uint64_t target = shadow + a.expected;
                 if ((a.inject & RR_INJECT_EXTRA_EXPECTED) && injected && step == 1) target += 1;
-                const WaitResult res = sig_wait(&a.sig[(uint64_t)slot * kSignalStride], target,
-                                                a.err, a.timeout_ticks);
+                const WaitResult res = sig_wait(wait_sig, target, a.err, a.timeout_ticks);
                 if (res.status == WAIT_TIMEOUT)
                     record_timeout(a.err, ctx, r, step, target, res.observed);
                 shadow = target;
@@ -261,7 +268,10 @@ __device__ __forceinline__ void barrier_body(const BarrierArgs& a, const uint32_
     }
     if (defer && a.nsteps == 1) arrive();
     if (lane == 0) {
-        if (!per_peer) a.shadow[slot] = shadow;
+        if (shared)
+            a.ctx_shadow[ctx] = shadow;  // every waiter of the context stores the same value
+        else if (!per_peer)
+            a.shadow[slot] = shadow;
         if (audit) a.early[slot] += early;
     }
     if (use_pp && peer_lane) *in_pp_shadow = pp_shadow;

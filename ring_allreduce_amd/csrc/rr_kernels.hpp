@@ -55,7 +55,8 @@ struct RingArgs {
     int32_t depth;       // lanes each workgroup interleaves hop by hop (1..kMaxDepth)
     int32_t nap;         // sleep between polls of a wait: 0 short, 1 medium, 2 long
     int32_t stream_in;   // loads of the predecessor's buffer are non-temporal
-    int32_t shared_sig;  // barrier: one signal per lane that all R ranks add to
+    int32_t shared_sig;  // barrier: one signal per lane that all R ranks add to (else
+                         // one per waiter that the R-1 others add to)
     int32_t pad;
     uint64_t* lane_sig;    // shared_sig: signal of lane l at lane_sig[l * kSignalStride]
     uint64_t* lane_shadow; // shared_sig: the lane's shadow (every rank's waiter tracks it)
@@ -144,7 +145,9 @@ struct BarrierArgs {
     uint64_t* stamps;    // optional: wall clock per (context, waiter): start, then each step
     uint32_t inject;
     int32_t audit;       // counting mode: also keep per-peer witnesses and count early passes
-    int32_t pad;
+    int32_t shared;      // counting mode: one signal per context that every waiter adds to
+    uint64_t* ctx_sig;   // shared: the context's signal at ctx_sig[ctx * kSignalStride]
+    uint64_t* ctx_shadow;// shared: the context's shadow (every waiter tracks it)
 };
 
 __device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }

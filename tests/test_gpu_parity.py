@@ -79,17 +79,18 @@ def test_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
                                       ("bf16", "sum")])
 @pytest.mark.parametrize("R,count,nslices,team", SMALL)
 @pytest.mark.parametrize("depth", [1, 2])
-def test_shared_lane_signal_small_ragged(rr, dtype, op, R, count, nslices, team, depth):
-    """A barrier per hop through one counting signal per lane that all R ranks add
-    to (a waiter expects R arrivals): the same bits as the oracle."""
+def test_waiter_signal_small_ragged(rr, dtype, op, R, count, nslices, team, depth):
+    """A barrier per hop through one counting signal per (lane, rank) that the
+    R-1 other ranks add to (RR_FLAG_WAITER_SIGNAL; the default is one signal per
+    lane): the same bits as the oracle."""
     if (nslices * team) % depth:
         pytest.skip("depth must divide the lanes")
-    log(f"case shared signal {dtype} {op} R={R} count={count} ns={nslices} team={team} "
+    log(f"case waiter signal {dtype} {op} R={R} count={count} ns={nslices} team={team} "
         f"depth={depth}")
     x = workloads.generate(R, count, dtype, DIST[dtype], R * 37 + count % 89)
     got = run_case(rr, x, dtype, op, nslices, sync="barrier", team=team, depth=depth,
-                   flags=rr.FLAG_SHARED_SIGNAL)
-    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"shared R={R} count={count}")
+                   flags=rr.FLAG_WAITER_SIGNAL)
+    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"waiter R={R} count={count}")
 
 
 # ------------------------------------- load policy (non-temporal incoming loads)
@@ -422,7 +423,7 @@ def test_rolling_counters_near_wrap(rr):
     x = workloads.generate(R, count, "fp32", "uniform_pm1", 9)
     expect = oracle_expect(x, "sum")
     rr.workspace_preset((1 << 64) - 3)
-    for sync, flags in (("p2p", 0), ("barrier", 0), ("barrier", rr.FLAG_SHARED_SIGNAL)):
+    for sync, flags in (("p2p", 0), ("barrier", 0), ("barrier", rr.FLAG_WAITER_SIGNAL)):
         log(f"case wrap sync={sync} flags={flags}")
         got = run_case(rr, x, "fp32", "sum", 4, sync=sync, flags=flags)
         assert_matches_oracle(got, expect, "fp32", f"wrap {sync} {flags}")
@@ -576,9 +577,9 @@ def test_full_fused_boundary(rr, w):
 
 @pytest.mark.parametrize("w", [workloads.R64_FP32_32MIB, workloads.r16_sweep(8, "sum", 16)],
                          ids=lambda w: w.name)
-def test_full_shared_lane_signal(rr, w):
-    """The barrier workloads with one shared counting signal per lane."""
-    _full_size(rr, w.with_(sync="barrier"), 4000, dict(flags=rr.FLAG_SHARED_SIGNAL))
+def test_full_waiter_signal(rr, w):
+    """The barrier workloads with one counting signal per (lane, rank)."""
+    _full_size(rr, w.with_(sync="barrier"), 4000, dict(flags=rr.FLAG_WAITER_SIGNAL))
 
 
 def test_full_cached_loads(rr):
@@ -666,14 +667,14 @@ def test_pieces_longer_than_one_descriptor(rr):
     assert_full_matches(recv, x, "fp32", "staged, 2 GiB per rank")
 
 
-@pytest.mark.parametrize("sync,flags", [("p2p", 0), ("barrier", 0), ("barrier", "shared")])
+@pytest.mark.parametrize("sync,flags", [("p2p", 0), ("barrier", 0), ("barrier", "waiter")])
 def test_hop_stamps(rr, sync, flags):
     """allreduce_ring_timed: the same bits as the oracle, and stamps that respect
     the hand-off order.  Per (lane, rank, hop): wait begins <= hop begins <= hop
     ends.  A hop begins only after the hop it waits for has begun: the
     predecessor's previous hop (P2P), every rank's previous hop (barrier)."""
     R, count, ns = 8, 8 * 4096 * 3 + 5, 3
-    f = rr.FLAG_SHARED_SIGNAL if flags == "shared" else 0
+    f = rr.FLAG_WAITER_SIGNAL if flags == "waiter" else 0
     log(f"case hop stamps sync={sync} flags={f}")
     x = workloads.generate(R, count, "fp32", "uniform_pm1", 61)
     slabs = to_slabs(rr, x, "fp32")

@@ -49,6 +49,49 @@ def test_counting_barrier_counts(rr, R, nctx, mode):
     b.close()
 
 
+@pytest.mark.parametrize("R,nctx", [(2, 1), (8, 4), (64, 8)])
+def test_shared_barrier_counts(rr, R, nctx):
+    """One signal per context that every waiter adds 1 to: it advances by R per
+    step, every waiter's shadow of it follows, and the per-waiter signals are
+    untouched."""
+    log(f"case shared barrier counts R={R} nctx={nctx}")
+    b = rr.CountingBarrier(64, 8)
+    b.run(R, 50, nctx, mode="shared")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    for ctx in range(nctx):
+        assert b.read(ctx, -1) == (50 * R, 50 * R)
+        assert b.read(ctx, 0) == (0, 0)
+    if nctx < 8:
+        assert b.read(nctx, -1) == (0, 0)
+    b.run(R, 7, nctx, mode="shared")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert b.read(0, -1) == (57 * R, 57 * R)
+    b.close()
+
+
+def test_shared_barrier_timeout_and_drop(rr):
+    """Shared layout: an expectation of R+1 per step, or a dropped arrival, times
+    out with one arrival missing; after reading the record and a reset the
+    barrier counts again."""
+    log("case shared barrier timeout")
+    b = rr.CountingBarrier(8, 2)
+    b.run(8, 5, 2, expected=9, mode="shared", timeout_ns=SHORT)
+    st, rec = rr.last_kernel_error()
+    assert st == rr.RR_ERR_TIMEOUT and rec["expected"] - rec["observed"] == 1
+    b.reset()
+    b.run(8, 3, 1, mode="shared", inject=rr.INJECT_DROP_ARRIVAL, timeout_ns=SHORT)
+    st, rec = rr.last_kernel_error()
+    assert st == rr.RR_ERR_TIMEOUT and rec["expected"] - rec["observed"] == 1
+    b.reset()
+    b.run(8, 5, 2, mode="shared")
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert b.read(1, -1) == (40, 40)
+    b.close()
+
+
 def test_counting_barrier_wraps(rr):
     log("case barrier wrap")
     b = rr.CountingBarrier(8, 1)
@@ -278,7 +321,7 @@ def test_plan_of_the_benchmark_workload(rr):
         rr.plan(64, 1 << 24, "fp32", 1024, sync="p2p")
 
 
-@pytest.mark.parametrize("mode", ["barrier", "per_peer", "p2p"])
+@pytest.mark.parametrize("mode", ["barrier", "shared", "per_peer", "p2p"])
 @pytest.mark.parametrize("R,nctx", [(2, 1), (5, 3), (16, 2), (64, 8)])
 def test_step_stamps_show_the_ordering(rr, mode, R, nctx):
     """In-kernel step times (one device-wide constant-rate clock): every waiter's
@@ -308,7 +351,7 @@ def test_step_stamps_show_the_ordering(rr, mode, R, nctx):
             assert (after[:, q] >= others).all(), f"waiter {q} left a step early"
     # the untimed run counts the same as the timed one
     for c in range(nctx):
-        for q in range(R):
+        for q in (range(R) if mode != "shared" else [-1]):
             v, sh = b.read(c, q)
             assert v == sh
     b.close()
