@@ -474,6 +474,7 @@ def main():
                    "op": w.op, "nslices": w.nslices, "sync": p["sync"], "team": p["team"],
                    "block": p["block"], "grid": p["grid"], "launches_per_step": p["launches"],
                    "rounds": p["rounds"], "depth": p["depth"], "stream_loads": p["stream_loads"],
+                   "alternate": p["alternate"],
                    "fused_boundary": bool(p["fused"]) if path == "ring" else False,
                    "algorithmic_bytes_per_step": B, "layout": args.layout,
                    "inputs_restored_before_each_call": path == "ring",
@@ -713,7 +714,8 @@ def r16_sweep(rr, torch, np, layout="separate"):
                                   "pct_of_peak": round(100 * B / ms / 1e6 / HBM_PEAK_GBS, 2),
                                   "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],
                                   "block": p["block"], "grid": p["grid"], "layout": layout,
-                                  "stream_loads": p["stream_loads"], "launches": p["launches"]}),
+                                  "stream_loads": p["stream_loads"], "alternate": p["alternate"],
+                                  "launches": p["launches"]}),
                       flush=True)
         del ranks, restore
         torch.cuda.empty_cache()

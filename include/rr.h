@@ -176,6 +176,13 @@ typedef enum {
 #define RR_FLAG_POLL_SLOW        0x400u /* ... about 4096 clocks (the default with a barrier
                                           whose hop moves 64 MiB or more).  At most one of
                                           the three poll flags (else RR_ERR_INVALID) */
+#define RR_FLAG_ASCENDING        0x1000u /* in-place ring and staged calls: every hop
+                                          (step) runs through its piece in ascending
+                                          order (see rr_plan_t.alternate).  Same
+                                          results */
+#define RR_FLAG_ALTERNATE        0x2000u /* ... every other hop (step) runs from the top
+                                          down, whatever the size (both flags
+                                          together: RR_ERR_INVALID) */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -225,6 +232,15 @@ typedef struct {
                             so the hint leaves the cache to the partials each rank
                             writes for its successor; when everything fits, it only
                             evicts lines that would have hit. */
+    int32_t alternate;   /* in-place ring: 1 if the even hops run through their piece
+                            from the top down (the odd ones bottom up), so that a hop
+                            first reads what its predecessor wrote last, which is the
+                            most likely to be still in the Infinity Cache.  By default
+                            when the R buffers together exceed half the cache
+                            (128 MiB); below that everything stays cached either way.
+                            The staged calls do the same with their odd steps, by the
+                            same rule on the R ranks' data; the AlltoAll never */
+    int32_t reserved;
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */
     uint64_t sub_len;    /* elements per team member */

@@ -56,6 +56,8 @@ FLAG_WAITER_SIGNAL = 0x800
 FLAG_POLL_FAST = 0x100
 FLAG_POLL_MEDIUM = 0x200
 FLAG_POLL_SLOW = 0x400
+FLAG_ASCENDING = 0x1000
+FLAG_ALTERNATE = 0x2000
 
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "fp32", torch.bfloat16: "bf16",
                  torch.float16: "fp16"}
@@ -75,7 +77,8 @@ class _Plan(ctypes.Structure):
                 ("xcd_map", ctypes.c_int32), ("cooperative", ctypes.c_int32),
                 ("resident_max", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("depth", ctypes.c_int32), ("fused", ctypes.c_int32),
-                ("stream_loads", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
+                ("stream_loads", ctypes.c_int32), ("alternate", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("chunk_len", ctypes.c_uint64),
                 ("slice_len", ctypes.c_uint64), ("sub_len", ctypes.c_uint64),
                 ("hbm_bytes", ctypes.c_uint64)]
 
@@ -189,13 +192,14 @@ def _stream_handle(stream):
 
 
 _LOADS = {"auto": 0, "stream": FLAG_STREAM_LOADS, "cached": FLAG_CACHED_LOADS}
+_ORDERS = {"auto": 0, "alternate": FLAG_ALTERNATE, "ascending": FLAG_ASCENDING}
 
 
 def _options(sync="auto", team=0, block=0, rounds=0, timeout_ns=0, inject=0, flags=0, depth=0,
-             fused=False, loads="auto"):
+             fused=False, loads="auto", order="auto"):
     if fused:
         flags |= FLAG_FUSED_BOUNDARY
-    flags |= _LOADS[loads]
+    flags |= _LOADS[loads] | _ORDERS[order]
     return Options(SYNCS[sync] if isinstance(sync, str) else int(sync), team, block, rounds,
                    timeout_ns, inject, flags, depth, 0)
 

@@ -57,7 +57,8 @@ struct RingArgs {
     int32_t stream_in;   // loads of the predecessor's buffer are non-temporal
     int32_t shared_sig;  // barrier: one signal per lane that all R ranks add to (else
                          // one per waiter that the R-1 others add to)
-    int32_t pad;
+    int32_t alternate;   // even hops run through their piece from the top down, so
+                         // that a hop first reads what its predecessor wrote last
     uint64_t* lane_sig;    // shared_sig: signal of lane l at lane_sig[l * kSignalStride]
     uint64_t* lane_shadow; // shared_sig: the lane's shadow (every rank's waiter tracks it)
     uint64_t* stamps;      // optional: wall clock per (lane, rank, hop): wait begins, hop
@@ -105,7 +106,7 @@ struct StagedArgs {
     int32_t k_last;
     int32_t xcd_map;
     int32_t aligned;       // every operand 16-byte aligned: the vector path
-    int32_t pad;
+    int32_t alternate;     // odd steps run through their piece from the top down
 };
 
 // The AlltoAll: one counting signal per receiver.

@@ -16,10 +16,12 @@
 // r in every chunk, so its hop-g input was written by workgroup (r-1, lane) at
 // hop g-1.  Every lane is an independent context with one 64-bit signal per
 // rank: after each hop the producer adds 1 to its successor's signal and the
-// consumer advances its shadow by 1 and waits (P2P); or, for a per-hop barrier,
-// every workgroup of the lane adds 1 to all R-1 other ranks' signals and each
-// waiter advances its shadow by R-1 (the counting barrier of the DeepEP pull
-// request "make the rail barrier a counting barrier", section "Fix").  A
+// consumer advances its shadow by 1 and waits (P2P).  For a per-hop barrier (the
+// counting barrier of the DeepEP pull request "make the rail barrier a counting
+// barrier", section "Fix") every workgroup of the lane adds 1 to the lane's one
+// shared signal and waits for it to advance by R, its own arrival included; or,
+// with one signal per waiter, adds 1 to the R-1 other ranks' signals and waits
+// for R-1 on its own.  A
 // workgroup serves `depth` lanes interleaved hop by hop (one lane's hand-off
 // completes while the other's hop runs) and `rounds` groups of lanes one after
 // another (so that the lanes in flight keep a hop's partials cached until the
@@ -38,7 +40,12 @@ namespace rr {
 // One hop of one workgroup over elements [lo, hi) of both buffers.  ReduceScatter:
 // dst = fold(src, dst).  AllGather: dst = src, bit for bit.  16-byte vectors,
 // U vectors per thread in flight, then a scalar tail (only at the ragged end).
-template <int DT, int OP, int BLOCK, int U, int AUX>
+// DESC runs the vectors from the top down.  The ring alternates (even hops top
+// down) once its buffers outgrow the caches: what a hop reads from its
+// predecessor's buffer was written one hop earlier in the opposite order, so
+// the lines written last -- the likeliest to be still in the Infinity Cache --
+// are read first, instead of every line waiting a whole hop.
+template <int DT, int OP, int BLOCK, int U, int AUX, bool DESC>
 __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void* dstbuf,
                                           void* dst2buf, uint64_t lo, uint64_t hi) {
     constexpr int ES = ElemBytes<DT>::value;
@@ -49,6 +56,9 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
     const __amdgpu_buffer_rsrc_t rs = incoming(sb, n * ES);
     u32x4* __restrict__ d = (u32x4*)((char*)dstbuf + lo * ES);
     u32x4* d2 = dst2buf ? (u32x4*)((char*)dst2buf + lo * ES) : nullptr;
+    // descending: vector k of the pass order is vector nv - 1 - k
+    const uint32_t top = nv - 1;
+#define RR_AT(k) (DESC ? top - (uint32_t)(k) : (uint32_t)(k))
     uint32_t i = threadIdx.x;
     if (reduce && d2) {
         // recvReduceCopySend: the finished chunk goes to the owner's buffer and on
@@ -56,43 +66,44 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, RR_AT(i + u * BLOCK));
 #pragma unroll
-            for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
+            for (int u = 0; u < U; ++u) y[u] = d[RR_AT(i + u * BLOCK)];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const u32x4 v = fold4<DT, OP>(x[u], y[u]);
-                d[i + u * BLOCK] = v;
-                d2[i + u * BLOCK] = v;
+                d[RR_AT(i + u * BLOCK)] = v;
+                d2[RR_AT(i + u * BLOCK)] = v;
             }
         }
         for (; i < nv; i += BLOCK) {
-            const u32x4 v = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
-            d[i] = v;
-            d2[i] = v;
+            const u32x4 v = fold4<DT, OP>(load_in<AUX>(rs, RR_AT(i)), d[RR_AT(i)]);
+            d[RR_AT(i)] = v;
+            d2[RR_AT(i)] = v;
         }
     } else if (reduce) {
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+            for (int u = 0; u < U; ++u) x[u] = load_in<AUX>(rs, RR_AT(i + u * BLOCK));
 #pragma unroll
-            for (int u = 0; u < U; ++u) y[u] = d[i + u * BLOCK];
+            for (int u = 0; u < U; ++u) y[u] = d[RR_AT(i + u * BLOCK)];
 #pragma unroll
-            for (int u = 0; u < U; ++u) d[i + u * BLOCK] = fold4<DT, OP>(x[u], y[u]);
+            for (int u = 0; u < U; ++u) d[RR_AT(i + u * BLOCK)] = fold4<DT, OP>(x[u], y[u]);
         }
-        for (; i < nv; i += BLOCK) d[i] = fold4<DT, OP>(load_in<AUX>(rs, i), d[i]);
+        for (; i < nv; i += BLOCK) d[RR_AT(i)] = fold4<DT, OP>(load_in<AUX>(rs, RR_AT(i)), d[RR_AT(i)]);
     } else {
         constexpr int UC = 2 * U;
         for (; i + (UC - 1) * BLOCK < nv; i += UC * BLOCK) {
             u32x4 x[UC];
 #pragma unroll
-            for (int u = 0; u < UC; ++u) x[u] = load_in<AUX>(rs, i + u * BLOCK);
+            for (int u = 0; u < UC; ++u) x[u] = load_in<AUX>(rs, RR_AT(i + u * BLOCK));
 #pragma unroll
-            for (int u = 0; u < UC; ++u) d[i + u * BLOCK] = x[u];
+            for (int u = 0; u < UC; ++u) d[RR_AT(i + u * BLOCK)] = x[u];
         }
-        for (; i < nv; i += BLOCK) d[i] = load_in<AUX>(rs, i);
+        for (; i < nv; i += BLOCK) d[RR_AT(i)] = load_in<AUX>(rs, RR_AT(i));
     }
+#undef RR_AT
     const uint64_t t = (uint64_t)nv * V + threadIdx.x;  // fewer than V elements remain
     if (t < n) {
         char* dp = (char*)dstbuf + (lo + t) * ES;
@@ -116,14 +127,19 @@ __device__ __forceinline__ void hop_piece(bool reduce, const void* srcbuf, void*
 
 template <int DT, int OP, int BLOCK, int U>
 __device__ __forceinline__ void hop_body(bool reduce, bool stream, const void* srcbuf,
-                                         void* dstbuf, void* dst2buf, uint64_t lo, uint64_t hi) {
+                                         void* dstbuf, void* dst2buf, uint64_t lo, uint64_t hi,
+                                         bool desc) {
     constexpr uint64_t kPiece = kPieceBytes / ElemBytes<DT>::value;  // elements, vector multiple
     for (uint64_t p = lo; p < hi; p += kPiece) {
         const uint64_t q = umin(p + kPiece, hi);
-        if (stream)
-            hop_piece<DT, OP, BLOCK, U, kAuxRingIncoming>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+        if (stream && desc)
+            hop_piece<DT, OP, BLOCK, U, kAuxRingIncoming, true>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+        else if (stream)
+            hop_piece<DT, OP, BLOCK, U, kAuxRingIncoming, false>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+        else if (desc)
+            hop_piece<DT, OP, BLOCK, U, kAuxDeviceScope, true>(reduce, srcbuf, dstbuf, dst2buf, p, q);
         else
-            hop_piece<DT, OP, BLOCK, U, kAuxDeviceScope>(reduce, srcbuf, dstbuf, dst2buf, p, q);
+            hop_piece<DT, OP, BLOCK, U, kAuxDeviceScope, false>(reduce, srcbuf, dstbuf, dst2buf, p, q);
     }
 }
 
@@ -235,7 +251,7 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
                 const uint64_t hi = umin(base + off_hi[p], a.count);
                 if (lo < hi && !skip)
                     hop_body<DT, OP, BLOCK, U>(reduce, a.stream_in != 0, a.bufs[r], a.bufs[succ],
-                                               dst2, lo, hi);
+                                               dst2, lo, hi, a.alternate != 0 && (g & 1) == 0);
 
                 if (g < a.g_last) {
                     if (!decided) {
@@ -293,8 +309,11 @@ __device__ __forceinline__ void ring_body(const RingArgs& a, const uint32_t gene
     }
 }
 
+// At least four waves per SIMD (two 512-thread or one 1024-thread workgroup per
+// CU, which every plan needs): the 16-bit kernels otherwise take more registers.
 template <int DT, int OP, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) ring_kernel(const RingArgs a) {
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+ring_kernel(const RingArgs a) {
     ring_body<DT, OP, BLOCK>(a, launch_generation(a.launch));
     leave_launch(a.launch);
 }

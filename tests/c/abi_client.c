@@ -31,6 +31,7 @@ static void layouts(void) {
     FIELD(rr_plan_t, grid); FIELD(rr_plan_t, launches); FIELD(rr_plan_t, xcd_map);
     FIELD(rr_plan_t, cooperative); FIELD(rr_plan_t, resident_max); FIELD(rr_plan_t, rounds);
     FIELD(rr_plan_t, depth); FIELD(rr_plan_t, fused); FIELD(rr_plan_t, stream_loads);
+    FIELD(rr_plan_t, alternate); FIELD(rr_plan_t, reserved);
     FIELD(rr_plan_t, chunk_len); FIELD(rr_plan_t, slice_len); FIELD(rr_plan_t, sub_len);
     FIELD(rr_plan_t, hbm_bytes);
     printf("\nrr_error_record_t size=%zu", sizeof(rr_error_record_t));

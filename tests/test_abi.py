@@ -199,6 +199,7 @@ def test_product_path_has_no_oracle_dependency():
     (0, dict(sync=4)), (2, dict(team=-1)), (3, dict(team=4097)), (4, dict(rounds=-1)),
     (5, dict(block=96)), (6, dict(sync=2)), (6, dict(team=65537)),
     (0, dict(flags=0x80 | 0x800)), (1, dict(flags=0x100 | 0x400)), (2, dict(flags=0x200 | 0x100)),
+    (0, dict(flags=0x1000 | 0x2000)), (1, dict(order="ascending", flags=0x2000)),
 ])
 def test_plan_query_rejects_what_the_call_rejects(rr, phase, opts):
     """The plan query checks options and sizes as the calls do, before any

@@ -1,8 +1,9 @@
 """Seeded random plans of the in-place ring against the CPU oracle.
 
 Each case draws ranks, a ragged size, element type, reduction, slices, hand-off
-mode, workgroup size, team, lanes per workgroup, rounds, boundary fusion, and
-whether the AllReduce runs as one call or as ReduceScatter then AllGather.  A
+mode, workgroup size, team, lanes per workgroup, rounds, boundary fusion, the
+hop direction (alternating or ascending), and whether the AllReduce runs as one
+call or as ReduceScatter then AllGather.  A
 combination the planner accepts must give the oracle's bits on every rank and
 leave the guard words around every rank buffer intact; a combination it rejects
 must be rejected by the call too, before anything is launched (an empty buffer
@@ -56,12 +57,13 @@ def _draw(k):
         split=bool(g.random() < 0.2),
     )
     case["fused"] = bool(not case["split"] and g.random() < 0.25)
+    case["order"] = str(g.choice(["auto", "alternate", "ascending"]))
     return case
 
 
 def _opts(c):
     o = dict(sync=c["sync"], block=c["block"], team=c["team"], depth=c["depth"],
-             rounds=c["rounds"])
+             rounds=c["rounds"], order=c["order"])
     if c["fused"]:
         o["fused"] = True
     return o

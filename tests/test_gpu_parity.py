@@ -109,6 +109,22 @@ def test_stream_loads_small_ragged(rr, dtype, op, R, count, nslices, team, sync)
         assert_matches_oracle(got, want, dtype, f"R={R} count={count} {opts}")
 
 
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("bf16", "max")])
+@pytest.mark.parametrize("R,count,nslices,team", [SMALL[0], SMALL[3], SMALL[5], SMALL[7]])
+@pytest.mark.parametrize("sync", ["p2p", "barrier", "launch"])
+def test_alternate_small_ragged(rr, dtype, op, R, count, nslices, team, sync):
+    """Small buffers run every hop ascending by default; forcing the alternating
+    direction (even hops top down) runs the other instantiation of every hop,
+    ragged ends included, with and without the fused boundary."""
+    log(f"case alternate {dtype} {op} R={R} count={count} ns={nslices} team={team} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], R * 43 + count % 83)
+    want = oracle_expect(x, op)
+    for opts in (dict(order="alternate"), dict(order="alternate", fused=True),
+                 dict(order="alternate", loads="stream")):
+        got = run_case(rr, x, dtype, op, nslices, sync=sync, team=team, **opts)
+        assert_matches_oracle(got, want, dtype, f"R={R} count={count} {opts}")
+
+
 def test_automatic_block_plan(rr):
     """Automatic workgroup size from the lane piece p, with the columns a
     512-thread plan would have: 128 if p <= 2 KiB, 256 if 16 KiB < p <= 32 KiB,
@@ -188,6 +204,24 @@ def test_stream_loads_plan(rr):
         rr.plan(8, 1024, "fp32", 1, flags=rr.FLAG_STREAM_LOADS | rr.FLAG_CACHED_LOADS)
 
 
+def test_alternate_plan(rr):
+    """Default: even hops top down once the R buffers exceed 128 MiB (half the
+    Infinity Cache); the flags force either order; the AlltoAll has no such
+    option."""
+    assert rr.plan(8, 4 << 20, "fp32", 4)["alternate"] == 0            # 128 MiB
+    assert rr.plan(8, (4 << 20) + 4, "fp32", 4)["alternate"] == 1
+    assert rr.plan(16, 1 << 18, "fp32", 4)["alternate"] == 0           # 16 MiB
+    assert rr.plan(16, 1 << 28, "fp32", 16, sync="barrier")["alternate"] == 1
+    assert rr.plan(64, 8 << 20, "fp32", 8)["alternate"] == 1
+    assert rr.plan(16, 1 << 10, "fp32", 4, order="alternate")["alternate"] == 1
+    assert rr.plan(8, 16 << 20, "fp32", 4, order="ascending")["alternate"] == 0
+    for phase in ("reduce_scatter", "all_gather"):
+        assert rr.plan(8, 16 << 20, "fp32", 4, phase=phase)["alternate"] == 1
+    assert rr.plan(8, 16 << 20, "fp32", 1, phase="alltoall")["alternate"] == 0
+    with pytest.raises(rr.RRError):
+        rr.plan(8, 1024, "fp32", 1, flags=rr.FLAG_ASCENDING | rr.FLAG_ALTERNATE)
+
+
 # ----------------------------------------------- several tiles, default plan
 
 MULTI = [(8, "fp32", "sum", (1 << 20) + 13, 4), (8, "bf16", "sum", (1 << 21) + 9, 8),
@@ -203,6 +237,17 @@ def test_multi_tile(rr, R, dtype, op, count, nslices, sync):
     x = workloads.generate(R, count, dtype, DIST[dtype], 100 + R)
     got = run_case(rr, x, dtype, op, nslices, sync=sync)
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"multi R={R}")
+
+
+@pytest.mark.parametrize("R,dtype,op,count,nslices", MULTI)
+@pytest.mark.parametrize("sync", ["p2p", "barrier"])
+def test_multi_tile_alternate(rr, R, dtype, op, count, nslices, sync):
+    log(f"case multi alternate R={R} {dtype} {op} count={count} ns={nslices} sync={sync}")
+    x = workloads.generate(R, count, dtype, DIST[dtype], 200 + R)
+    want = oracle_expect(x, op)
+    for order in ("alternate", "ascending"):
+        got = run_case(rr, x, dtype, op, nslices, sync=sync, order=order)
+        assert_matches_oracle(got, want, dtype, f"multi {order} R={R}")
 
 
 @pytest.mark.parametrize("R,dtype,op,count,nslices", MULTI)
