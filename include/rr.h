@@ -176,13 +176,13 @@ typedef enum {
 #define RR_FLAG_POLL_SLOW        0x400u /* ... about 4096 clocks (the default with a barrier
                                           whose hop moves 64 MiB or more).  At most one of
                                           the three poll flags (else RR_ERR_INVALID) */
-#define RR_FLAG_ASCENDING        0x1000u /* in-place ring and staged calls: every hop
-                                          (step) runs through its piece in ascending
-                                          order (see rr_plan_t.alternate).  Same
-                                          results */
-#define RR_FLAG_ALTERNATE        0x2000u /* ... every other hop (step) runs from the top
+#define RR_FLAG_ASCENDING        0x1000u /* in-place ring: every hop runs through its
+                                          piece in ascending order (see
+                                          rr_plan_t.alternate).  Same results */
+#define RR_FLAG_ALTERNATE        0x2000u /* in-place ring: the even hops run from the top
                                           down, whatever the size (both flags
-                                          together: RR_ERR_INVALID) */
+                                          together: RR_ERR_INVALID; the other calls
+                                          ignore both) */
 #define RR_FLAG_COOPERATIVE      0x4u /* launch the persistent kernel with
                                          hipLaunchCooperativeKernel (co-residency
                                          guaranteed by the runtime; otherwise the
@@ -238,8 +238,7 @@ typedef struct {
                             most likely to be still in the Infinity Cache.  By default
                             when the R buffers together exceed half the cache
                             (128 MiB); below that everything stays cached either way.
-                            The staged calls do the same with their odd steps, by the
-                            same rule on the R ranks' data; the AlltoAll never */
+                            Other calls: always 0 */
     int32_t reserved;
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */

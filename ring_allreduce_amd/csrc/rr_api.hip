@@ -452,7 +452,13 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
             block = kSmallBlock;
     }
     p->block = block;
-    const void* kernel = (const void*)pick_ring_kernel(dt, op, block);
+    // even hops top down once the buffers outgrow half the Infinity Cache: a hop
+    // then reads first what its predecessor wrote last (A/B over R = 2-64 and
+    // 1 MiB-1 GiB per rank: +0.5-3% above, up to 3% slower at 64-128 MiB in all).
+    // It is a kernel of its own, so that the smaller calls keep the leaner code.
+    p->alternate = (flags & RR_FLAG_ALTERNATE) ||
+                   (!(flags & RR_FLAG_ASCENDING) && (uint64_t)R * nbytes > kInfinityCacheBytes / 2);
+    const void* kernel = (const void*)pick_ring_kernel(dt, op, block, p->alternate != 0);
     p->resident_max = resident_limit(d, kernel, block);
     // Columns on the XCD map are padded to a multiple of 8 (idle columns exit).
     p->xcd_map = (flags & RR_FLAG_NO_XCD_MAP) ? 0 : 1;
@@ -479,11 +485,6 @@ static rr_status_t make_plan(const DeviceState* d, int R, size_t count, int dt, 
     if (flags & RR_FLAG_POLL_SLOW) p->nap = 2;
     p->stream_in = (flags & RR_FLAG_STREAM_LOADS) ||
                    (!(flags & RR_FLAG_CACHED_LOADS) && (uint64_t)R * nbytes > kInfinityCacheBytes);
-    // even hops top down once the buffers outgrow half the Infinity Cache: a hop
-    // then reads first what its predecessor wrote last (A/B over R = 2-64 and
-    // 1 MiB-1 GiB per rank: +0.5-3% above, up to 3% slower at 64-128 MiB in all)
-    p->alternate = (flags & RR_FLAG_ALTERNATE) ||
-                   (!(flags & RR_FLAG_ASCENDING) && (uint64_t)R * nbytes > kInfinityCacheBytes / 2);
     return RR_OK;
 }
 
@@ -536,11 +537,10 @@ static rr_status_t run_ring(void* const* bufs, int R, size_t count, int dt, int 
     a.shared_sig = p.sync == RR_SYNC_BARRIER && !(opt && (opt->flags & RR_FLAG_WAITER_SIGNAL)) ? 1 : 0;
     a.lane_sig = d->lane_sig;
     a.lane_shadow = d->lane_shadow;
-    a.alternate = p.alternate;
     a.stamps = stamps;
     a.xcd_map = p.xcd_map;
     a.inject = opt ? opt->inject : 0;
-    RingKernel k = pick_ring_kernel(dt, op, p.block);
+    RingKernel k = pick_ring_kernel(dt, op, p.block, p.alternate != 0);
     hipStream_t s = (hipStream_t)stream;
     if (p.sync == RR_SYNC_LAUNCH) {
         a.sync = SYNC_NONE;
@@ -586,11 +586,7 @@ static rr_status_t make_staged_plan(const DeviceState* d, int R, uint64_t n, int
     p->block = kStagedBlock;
     p->fuse = 0;
     p->stream_in = 0;
-    {   // odd steps top down once the R ranks' data outgrow half the Infinity Cache
-        const uint64_t all = (mode == MODE_ALLREDUCE ? (uint64_t)R : (uint64_t)R * R) * n * es;
-        p->alternate = (flags & RR_FLAG_ALTERNATE) ||
-                       (!(flags & RR_FLAG_ASCENDING) && all > kInfinityCacheBytes / 2);
-    }
+    p->alternate = 0;
     p->chunk_len = mode == MODE_ALLREDUCE ? round_up(ceil_div(n, (uint64_t)R), V) : n;
     p->slice_len = round_up(ceil_div(p->chunk_len, (uint64_t)nslices), V);
     p->g_first = 0;
@@ -850,7 +846,6 @@ static rr_status_t run_staged(const void* const* send, void* const* recv, int R,
     a.mode = mode;
     a.xcd_map = p.xcd_map;
     a.aligned = mode == MODE_ALLREDUCE || (n * es) % 16 == 0;
-    a.alternate = p.alternate;
     StagedKernel k = pick_staged_kernel(dt, mode == MODE_AG ? RR_SUM : op);
     if (p.sync == RR_SYNC_LAUNCH) {
         for (int step = p.g_first; step <= p.g_last; ++step) {

@@ -57,8 +57,7 @@ struct RingArgs {
     int32_t stream_in;   // loads of the predecessor's buffer are non-temporal
     int32_t shared_sig;  // barrier: one signal per lane that all R ranks add to (else
                          // one per waiter that the R-1 others add to)
-    int32_t alternate;   // even hops run through their piece from the top down, so
-                         // that a hop first reads what its predecessor wrote last
+    int32_t pad;
     uint64_t* lane_sig;    // shared_sig: signal of lane l at lane_sig[l * kSignalStride]
     uint64_t* lane_shadow; // shared_sig: the lane's shadow (every rank's waiter tracks it)
     uint64_t* stamps;      // optional: wall clock per (lane, rank, hop): wait begins, hop
@@ -106,7 +105,7 @@ struct StagedArgs {
     int32_t k_last;
     int32_t xcd_map;
     int32_t aligned;       // every operand 16-byte aligned: the vector path
-    int32_t alternate;     // odd steps run through their piece from the top down
+    int32_t pad;
 };
 
 // The AlltoAll: one counting signal per receiver.
@@ -314,7 +313,8 @@ typedef void (*BarrierKernel)(BarrierArgs);
 typedef void (*FillKernel)(uint64_t*, uint64_t, uint64_t, uint64_t);
 typedef void (*CopyKernel)(const u32x4*, u32x4*, uint64_t, const uint8_t*, uint8_t*, uint32_t);
 
-RingKernel pick_ring_kernel(int dt, int op, int block);  // block 128, 256, 512 or 1024
+// block 128, 256, 512 or 1024; alternate: the kernel whose even hops run top down
+RingKernel pick_ring_kernel(int dt, int op, int block, bool alternate);
 StagedKernel pick_staged_kernel(int dt, int op);
 AlltoallKernel pick_alltoall_kernel(int elem_bytes);     // 2 or 4
 BarrierKernel barrier_kernel_handle();

@@ -1,7 +1,5 @@
 // rr_staged_kernel.hip -- the staged loop: the ring as the primitives of one
 // rank, out of place, with receive slots and credits.
-#include <type_traits>
-
 #include "rr_kernels.hpp"
 
 namespace rr {
@@ -42,7 +40,7 @@ template <int P> struct Prim {
 // local (the rank's input), out (its output), next (the successor's slot).
 // Output stores are non-temporal: nothing in the collective reads them back,
 // while the successor reads `next` one step later (measured: 1-3% at 8 ranks).
-template <int DT, int OP, int BLOCK, int P, bool DESC>
+template <int DT, int OP, int BLOCK, int P>
 __device__ __forceinline__ void staged_piece(const void* in, const void* local, void* out,
                                              void* next, uint64_t n, bool aligned) {
     using Q = Prim<P>;
@@ -57,19 +55,16 @@ __device__ __forceinline__ void staged_piece(const void* in, const void* local, 
         const u32x4* __restrict__ lp = (const u32x4*)local;
         u32x4* __restrict__ op = (u32x4*)out;
         u32x4* __restrict__ np = (u32x4*)next;
-        // DESC: vector k of the pass order is vector nv - 1 - k (as in the ring)
-        const uint32_t top = nv - 1;
-#define RR_AT(k) (DESC ? top - (uint32_t)(k) : (uint32_t)(k))
         uint32_t i = threadIdx.x;
         for (; i + (U - 1) * BLOCK < nv; i += U * BLOCK) {
             u32x4 x[U], y[U];
             if constexpr (Q::in) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) x[u] = load_in(rs, RR_AT(i + u * BLOCK));
+                for (int u = 0; u < U; ++u) x[u] = load_in(rs, i + u * BLOCK);
             }
             if constexpr (Q::local) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) y[u] = lp[RR_AT(i + u * BLOCK)];
+                for (int u = 0; u < U; ++u) y[u] = lp[i + u * BLOCK];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -77,19 +72,18 @@ __device__ __forceinline__ void staged_piece(const void* in, const void* local, 
                 if constexpr (Q::reduce) v = fold4<DT, OP>(x[u], y[u]);
                 else if constexpr (Q::in) v = x[u];
                 else v = y[u];
-                if constexpr (Q::out) __builtin_nontemporal_store(v, &op[RR_AT(i + u * BLOCK)]);
-                if constexpr (Q::send) np[RR_AT(i + u * BLOCK)] = v;
+                if constexpr (Q::out) __builtin_nontemporal_store(v, &op[i + u * BLOCK]);
+                if constexpr (Q::send) np[i + u * BLOCK] = v;
             }
         }
         for (; i < nv; i += BLOCK) {
             u32x4 v;
-            if constexpr (Q::reduce) v = fold4<DT, OP>(load_in(rs, RR_AT(i)), lp[RR_AT(i)]);
-            else if constexpr (Q::in) v = load_in(rs, RR_AT(i));
-            else v = lp[RR_AT(i)];
-            if constexpr (Q::out) __builtin_nontemporal_store(v, &op[RR_AT(i)]);
-            if constexpr (Q::send) np[RR_AT(i)] = v;
+            if constexpr (Q::reduce) v = fold4<DT, OP>(load_in(rs, i), lp[i]);
+            else if constexpr (Q::in) v = load_in(rs, i);
+            else v = lp[i];
+            if constexpr (Q::out) __builtin_nontemporal_store(v, &op[i]);
+            if constexpr (Q::send) np[i] = v;
         }
-#undef RR_AT
         done = (uint64_t)nv * V;
     }
     // element by element: the ragged end, or everything when an operand is not
@@ -117,15 +111,15 @@ __device__ __forceinline__ void staged_piece(const void* in, const void* local, 
 }
 
 // A piece longer than one buffer descriptor can cover is moved in parts.
-template <int DT, int OP, int BLOCK, int P, bool DESC>
+template <int DT, int OP, int BLOCK, int P>
 __device__ __forceinline__ void staged_move(const char* in, const char* local, char* out, char* next,
                                             uint64_t n, bool aligned) {
     constexpr int ES = ElemBytes<DT>::value;
     constexpr uint64_t kPart = kPieceBytes / ES;
     for (uint64_t p = 0; p < n; p += kPart) {
         const uint64_t m = umin(kPart, n - p);
-        staged_piece<DT, OP, BLOCK, P, DESC>(in + p * ES, local + p * ES, out + p * ES,
-                                             next + p * ES, m, aligned);
+        staged_piece<DT, OP, BLOCK, P>(in + p * ES, local + p * ES, out + p * ES, next + p * ES, m,
+                                       aligned);
     }
 }
 
@@ -215,30 +209,21 @@ __device__ __forceinline__ void staged_body(const StagedArgs& a, const uint32_t 
             char* op = (char*)a.recv[r] + (obase + lo) * ES;
             const uint64_t m = hi - lo;
             const bool al = a.aligned != 0;
-            // odd steps top down when alternating: a step reads first what its
-            // predecessor wrote last (see the in-place ring)
-            auto move = [&](auto desc) {
-                constexpr bool D = decltype(desc)::value;
-                if (a.mode == MODE_ALLREDUCE) {
-                    if (k == 0) staged_move<DT, OP, BLOCK, P_SEND, D>(in, lp, op, next, m, al);
-                    else if (k < R - 1) staged_move<DT, OP, BLOCK, P_RRS, D>(in, lp, op, next, m, al);
-                    else if (k == R - 1) staged_move<DT, OP, BLOCK, P_RRCS, D>(in, lp, op, next, m, al);
-                    else if (k < K) staged_move<DT, OP, BLOCK, P_RCS, D>(in, lp, op, next, m, al);
-                    else staged_move<DT, OP, BLOCK, P_RECV, D>(in, lp, op, next, m, al);
-                } else if (a.mode == MODE_RS) {
-                    if (k == 0) staged_move<DT, OP, BLOCK, P_SEND, D>(in, lp, op, next, m, al);
-                    else if (k < K) staged_move<DT, OP, BLOCK, P_RRS, D>(in, lp, op, next, m, al);
-                    else staged_move<DT, OP, BLOCK, P_RRC, D>(in, lp, op, next, m, al);
-                } else {
-                    if (k == 0) staged_move<DT, OP, BLOCK, P_CS, D>(in, lp, op, next, m, al);
-                    else if (k < K) staged_move<DT, OP, BLOCK, P_RCS, D>(in, lp, op, next, m, al);
-                    else staged_move<DT, OP, BLOCK, P_RECV, D>(in, lp, op, next, m, al);
-                }
-            };
-            if (a.alternate != 0 && (k & 1) == 1)
-                move(std::true_type{});
-            else
-                move(std::false_type{});
+            if (a.mode == MODE_ALLREDUCE) {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_SEND>(in, lp, op, next, m, al);
+                else if (k < R - 1) staged_move<DT, OP, BLOCK, P_RRS>(in, lp, op, next, m, al);
+                else if (k == R - 1) staged_move<DT, OP, BLOCK, P_RRCS>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RCS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RECV>(in, lp, op, next, m, al);
+            } else if (a.mode == MODE_RS) {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_SEND>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RRS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RRC>(in, lp, op, next, m, al);
+            } else {
+                if (k == 0) staged_move<DT, OP, BLOCK, P_CS>(in, lp, op, next, m, al);
+                else if (k < K) staged_move<DT, OP, BLOCK, P_RCS>(in, lp, op, next, m, al);
+                else staged_move<DT, OP, BLOCK, P_RECV>(in, lp, op, next, m, al);
+            }
         }
 
         if (synced) {
@@ -276,11 +261,8 @@ __device__ __forceinline__ void staged_body(const StagedArgs& a, const uint32_t 
     }  // rounds
 }
 
-// At least four waves per SIMD: two 512-thread workgroups per CU, which the plans
-// count on (the 16-bit kernels otherwise take more registers).
 template <int DT, int OP, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
-staged_kernel(const StagedArgs a) {
+__global__ void __launch_bounds__(BLOCK) staged_kernel(const StagedArgs a) {
     staged_body<DT, OP, BLOCK>(a, launch_generation(a.launch));
     leave_launch(a.launch);
 }

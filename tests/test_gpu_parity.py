@@ -206,8 +206,8 @@ def test_stream_loads_plan(rr):
 
 def test_alternate_plan(rr):
     """Default: even hops top down once the R buffers exceed 128 MiB (half the
-    Infinity Cache); the flags force either order; the AlltoAll has no such
-    option."""
+    Infinity Cache); the flags force either order; the staged kernel and the
+    AlltoAll always run ascending."""
     assert rr.plan(8, 4 << 20, "fp32", 4)["alternate"] == 0            # 128 MiB
     assert rr.plan(8, (4 << 20) + 4, "fp32", 4)["alternate"] == 1
     assert rr.plan(16, 1 << 18, "fp32", 4)["alternate"] == 0           # 16 MiB
@@ -217,7 +217,9 @@ def test_alternate_plan(rr):
     assert rr.plan(8, 16 << 20, "fp32", 4, order="ascending")["alternate"] == 0
     for phase in ("reduce_scatter", "all_gather"):
         assert rr.plan(8, 16 << 20, "fp32", 4, phase=phase)["alternate"] == 1
-    assert rr.plan(8, 16 << 20, "fp32", 1, phase="alltoall")["alternate"] == 0
+    for phase in ("allreduce_staged", "reduce_scatter_blocks", "all_gather_blocks", "alltoall"):
+        assert rr.plan(8, 16 << 20, "fp32", 1, phase=phase)["alternate"] == 0
+        assert rr.plan(8, 16 << 20, "fp32", 1, phase=phase, order="alternate")["alternate"] == 0
     with pytest.raises(rr.RRError):
         rr.plan(8, 1024, "fp32", 1, flags=rr.FLAG_ASCENDING | rr.FLAG_ALTERNATE)
 

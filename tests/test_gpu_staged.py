@@ -59,53 +59,6 @@ def test_staged_small_ragged(rr, dtype, op, R, count, nslices, sync):
     assert_matches_oracle(got, oracle_expect(x, op), dtype, f"staged R={R} count={count}")
 
 
-@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("fp32", "sum"), ("bf16", "min"),
-                                      ("fp16", "prod")])
-@pytest.mark.parametrize("R,count,nslices", SMALL)
-@pytest.mark.parametrize("sync", ["p2p", "launch"])
-def test_staged_alternate_small_ragged(rr, dtype, op, R, count, nslices, sync):
-    """Small buffers run every step ascending by default; forcing the alternating
-    direction (odd steps top down) runs the other instantiation of every
-    primitive over the same ragged cases."""
-    log(f"case staged alternate {dtype} {op} R={R} count={count} ns={nslices} sync={sync}")
-    x = workloads.generate(R, count, dtype, _dist(dtype, op), R * 17 + count % 79)
-    got = _staged(rr, x, dtype, op, nslices, sync=sync, order="alternate")
-    assert_matches_oracle(got, oracle_expect(x, op), dtype, f"staged alternate R={R}")
-
-
-@pytest.mark.parametrize("R,n", [(3, 64), (8, 4096), (8, 4099), (16, 333)])
-@pytest.mark.parametrize("sync", ["p2p", "launch"])
-def test_blocks_alternate(rr, R, n, sync):
-    """The standalone collectives with the alternating direction forced."""
-    log(f"case blocks alternate R={R} n={n} sync={sync}")
-    x = workloads.generate(R, R * n, "fp32", "uniform_pm1", 90 + R)
-    recv = rr.reduce_scatter(_blocks_send(x, "fp32"), None, "sum", 2, sync=sync, order="alternate")
-    torch.cuda.synchronize()
-    rr.check_kernel_error()
-    want, _ = oracle.reduce_scatter_nccl(x, "sum")
-    assert_matches_oracle([to_host(t, "fp32") for t in recv], want, "fp32", f"rs alternate R={R}")
-    y = workloads.generate(R, n, "bf16", "bits", 95 + R)
-    recv = rr.all_gather(_blocks_send(y, "bf16"), None, 3, sync=sync, order="alternate")
-    torch.cuda.synchronize()
-    rr.check_kernel_error()
-    want = np.concatenate([a.view(RAW_NP["bf16"]) for a in y])
-    for t in recv:
-        assert np.array_equal(to_host(t, "bf16"), want)
-
-
-def test_staged_alternate_plan(rr):
-    """The staged kernel alternates by the in-place ring's rule, on the R ranks'
-    whole data (R x n elements for the staged AllReduce, R x R x n for the
-    standalone collectives)."""
-    ph = "allreduce_staged"
-    assert rr.plan(8, 4 << 20, "fp32", 4, phase=ph)["alternate"] == 0            # 128 MiB
-    assert rr.plan(8, (4 << 20) + 4, "fp32", 4, phase=ph)["alternate"] == 1
-    assert rr.plan(8, 1 << 19, "fp32", 1, phase="reduce_scatter_blocks")["alternate"] == 0
-    assert rr.plan(8, (1 << 19) + 4, "fp32", 1, phase="all_gather_blocks")["alternate"] == 1
-    assert rr.plan(8, 1024, "fp32", 1, phase=ph, order="alternate")["alternate"] == 1
-    assert rr.plan(8, 16 << 20, "fp32", 1, phase=ph, order="ascending")["alternate"] == 0
-
-
 def test_staged_equals_the_oracles_staged_loop(rr):
     R, count = 6, 6 * 1000 + 9
     x = workloads.generate(R, count, "bf16", "normal", 61)
