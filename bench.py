@@ -461,6 +461,7 @@ def main():
                "gpu_matches_oracle_bitwise": bool(ok),
                "compared": "every element of every rank: the output of the last timed call",
                "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1)
         log(f"cpu baseline: {cpu}")
     run.release()
 
