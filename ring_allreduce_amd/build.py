@@ -11,11 +11,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librr.so")
-# one translation unit per kernel family, and the host side with the C ABI
+# one translation unit per kernel family (the in-place ring: one per element
+# type), and the host side with the C ABI
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("rr_ring_kernel.hip", "rr_staged_kernel.hip", "rr_aux_kernels.hip", "rr_api.hip")]
+           ("rr_ring_i32.hip", "rr_ring_f32.hip", "rr_ring_bf16.hip", "rr_ring_f16.hip",
+            "rr_staged_kernel.hip", "rr_aux_kernels.hip", "rr_api.hip")]
 HEADERS = [os.path.join(CSRC, "rr_device.hpp"), os.path.join(CSRC, "rr_kernels.hpp"),
-           os.path.join(ROOT, "include", "rr.h")]
+           os.path.join(CSRC, "rr_ring_kernel.hpp"), os.path.join(ROOT, "include", "rr.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -313,8 +313,21 @@ typedef void (*BarrierKernel)(BarrierArgs);
 typedef void (*FillKernel)(uint64_t*, uint64_t, uint64_t, uint64_t);
 typedef void (*CopyKernel)(const u32x4*, u32x4*, uint64_t, const uint8_t*, uint8_t*, uint32_t);
 
-// block 128, 256, 512 or 1024; alternate: the kernel whose even hops run top down
-RingKernel pick_ring_kernel(int dt, int op, int block, bool alternate);
+// block 128, 256, 512 or 1024; alternate: the kernel whose even hops run top down.
+// One translation unit per element type holds the ring kernels (rr_ring_<type>.hip).
+RingKernel pick_ring_kernel_i32(int op, int block, bool alternate);
+RingKernel pick_ring_kernel_f32(int op, int block, bool alternate);
+RingKernel pick_ring_kernel_bf16(int op, int block, bool alternate);
+RingKernel pick_ring_kernel_f16(int op, int block, bool alternate);
+inline RingKernel pick_ring_kernel(int dt, int op, int block, bool alternate) {
+    switch (dt) {
+        case RR_INT32: return pick_ring_kernel_i32(op, block, alternate);
+        case RR_FP32: return pick_ring_kernel_f32(op, block, alternate);
+        case RR_BF16: return pick_ring_kernel_bf16(op, block, alternate);
+        case RR_FP16: return pick_ring_kernel_f16(op, block, alternate);
+        default: return nullptr;
+    }
+}
 StagedKernel pick_staged_kernel(int dt, int op);
 AlltoallKernel pick_alltoall_kernel(int elem_bytes);     // 2 or 4
 BarrierKernel barrier_kernel_handle();

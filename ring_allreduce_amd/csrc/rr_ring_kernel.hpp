@@ -1,5 +1,8 @@
-// rr_ring_kernel.hip -- the in-place ring kernel (ReduceScatter, AllGather and
-// the AllReduce that chains them) over virtual ranks on one MI355X.
+// rr_ring_kernel.hpp -- the in-place ring kernel (ReduceScatter, AllGather and
+// the AllReduce that chains them) over virtual ranks on one MI355X.  Included by
+// one translation unit per element type (rr_ring_<type>.hip), which compile in
+// parallel: each holds the 32 kernels of its type (4 reductions x 4 workgroup
+// sizes x hop order).
 //
 // Method (post "Why AllReduce = ReduceScatter + AllGather -- with NCCL Ring
 // AllReduce", loosp.cn, sections 4-6): global hop g = 1 .. 2(R-1).  Hops 1..R-1
@@ -33,6 +36,8 @@
 // the hazard the same pull request describes for anonymous counting (section
 // "Scoped to the rail team": a count says that enough arrived, not who) -- and
 // the consumer of that teammate's sub-range would read stale data.
+#pragma once
+
 #include "rr_kernels.hpp"
 
 namespace rr {
@@ -355,20 +360,11 @@ static RingKernel ring_kernel_for_op(int op, int block) {
     }
 }
 
-template <bool ALT>
-static RingKernel ring_kernel_for_type(int dt, int op, int block) {
-    switch (dt) {
-        case RR_INT32: return ring_kernel_for_op<DT_I32, ALT>(op, block);
-        case RR_FP32: return ring_kernel_for_op<DT_F32, ALT>(op, block);
-        case RR_BF16: return ring_kernel_for_op<DT_BF16, ALT>(op, block);
-        case RR_FP16: return ring_kernel_for_op<DT_F16, ALT>(op, block);
-        default: return nullptr;
-    }
-}
-
-RingKernel pick_ring_kernel(int dt, int op, int block, bool alternate) {
-    return alternate ? ring_kernel_for_type<true>(dt, op, block)
-                     : ring_kernel_for_type<false>(dt, op, block);
+// The kernel for (op, block, hop order) of element type DT.
+template <int DT>
+RingKernel ring_kernel_for_type(int op, int block, bool alternate) {
+    return alternate ? ring_kernel_for_op<DT, true>(op, block)
+                     : ring_kernel_for_op<DT, false>(op, block);
 }
 
 }  // namespace rr
