@@ -208,7 +208,7 @@ typedef struct {
     uint32_t inject;     /* RR_INJECT_* */
     uint32_t flags;      /* RR_FLAG_* */
     int32_t depth;       /* lanes each workgroup interleaves hop by hop, 1..4; 0 = choose */
-    int32_t reserved;
+    int32_t reserved;    /* 0 */
 } rr_options_t;
 
 /* What a call will run (rr_plan_query). */
@@ -239,7 +239,7 @@ typedef struct {
                             when the R buffers together exceed half the cache
                             (128 MiB); below that everything stays cached either way.
                             Other calls: always 0 */
-    int32_t reserved;
+    int32_t reserved;    /* 0 */
     uint64_t chunk_len;  /* elements */
     uint64_t slice_len;  /* elements */
     uint64_t sub_len;    /* elements per team member */
@@ -258,7 +258,7 @@ typedef struct {
     int32_t waiter;    /* its virtual rank */
     int32_t hop;       /* hop (or barrier step) it was about to start */
     int32_t peer;      /* the peer that did not arrive (per-peer slots), else -1 */
-    int32_t reserved;
+    int32_t reserved;    /* 0 */
     uint64_t expected; /* signal value it waited for */
     uint64_t observed; /* last value it read; expected - observed are missing */
 } rr_error_record_t;
