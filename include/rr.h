@@ -258,7 +258,7 @@ typedef struct {
     int32_t waiter;    /* its virtual rank */
     int32_t hop;       /* hop (or barrier step) it was about to start */
     int32_t peer;      /* the peer that did not arrive (per-peer slots), else -1 */
-    int32_t reserved;    /* 0 */
+    int32_t reserved;  /* 0 */
     uint64_t expected; /* signal value it waited for */
     uint64_t observed; /* last value it read; expected - observed are missing */
 } rr_error_record_t;
