@@ -1,8 +1,8 @@
 /*
  * exhaustive_hop.c -- TEST HELPER: every ordered pair of 16-bit operands
- * through the CPU oracle's one-hop SUM fold, against a reference written here.
+ * through the CPU oracle's one-hop fold, against a reference written here.
  *
- * Usage: exhaustive_hop ORACLE_SO DTYPE DECODE_TABLE THREADS [STEP]
+ * Usage: exhaustive_hop ORACLE_SO DTYPE DECODE_TABLE THREADS [STEP [OP]]
  *   ORACLE_SO     path of the oracle's shared library (loaded with dlopen; only
  *                 its ro_allreduce entry point is called)
  *   DTYPE         2 = bfloat16, 3 = binary16 (the oracle's dtype codes)
@@ -11,6 +11,7 @@
  *   THREADS       worker threads
  *   STEP          check the first operands 0, STEP, 2*STEP, ... only (default 1:
  *                 all 65536 of them, i.e. all 2^32 ordered pairs)
+ *   OP            0 = SUM (default), 1 = MAX, 2 = MIN, 3 = PROD (the oracle's codes)
  *
  * The per-hop fold of a 16-bit SUM is the exact sum of the two operands rounded
  * once to the format, nearest even (the post "Why AllReduce = ReduceScatter +
@@ -20,12 +21,17 @@
  * rounds that sum to the format by integer operations on its bits.  Rounding
  * the exact sum first to binary64 and then to p significant bits equals one
  * rounding because 53 >= 2p + 2 (p = 8 or 11).  Any NaN result is the format's
- * canonical quiet NaN (0x7FC0, 0x7E00).
+ * canonical quiet NaN (0x7FC0, 0x7E00).  PROD: the product of the two decoded
+ * values, exact in binary64 (at most 2p <= 22 significant bits), rounded once
+ * the same way.  MAX and MIN select, with no arithmetic: the local operand if it
+ * compares greater (less) than the incoming one, else the incoming one, so ties,
+ * signed zeros and NaNs resolve by that rule, bit for bit.
  *
  * For each first operand a (one oracle call per a), rank 0 holds a in all 65536
  * positions and rank 1 holds every pattern b once; with R = 2 each position is
- * folded exactly once (incoming a into local b in the first chunk, incoming b
- * into local a in the second), and both ranks end with the folded value.
+ * folded exactly once (incoming a into local b in the first chunk, positions
+ * below 32768; incoming b into local a in the second), and both ranks end with
+ * the folded value.
  *
  * Prints "pairs N mismatches M" and, on a mismatch, the first one.
  */
@@ -92,6 +98,18 @@ static uint16_t round_to_format(double s)
 }
 
 static int g_step = 1;
+static int g_op = 0;
+
+/* The folded pattern at position b of the call for first operand a. */
+static uint16_t reference(int a, int b)
+{
+    if (g_op == 0) return round_to_format(g_value[a] + g_value[b]);
+    if (g_op == 3) return round_to_format(g_value[a] * g_value[b]);
+    const int in = b < 32768 ? a : b, lo = b < 32768 ? b : a;
+    const double vin = g_value[in], vlo = g_value[lo];
+    const int local_wins = g_op == 1 ? vlo > vin : vlo < vin;
+    return (uint16_t)(local_wins ? lo : in);
+}
 
 typedef struct {
     int first, last; /* first operands [first, last), taken every g_step */
@@ -118,12 +136,12 @@ static void *worker(void *arg)
             r0[b] = (uint16_t)a;
             r1[b] = (uint16_t)b;
         }
-        if (g_allreduce(bufs, 2, 65536, g_dtype, 0 /* SUM */, NULL) != 0) {
+        if (g_allreduce(bufs, 2, 65536, g_dtype, g_op, NULL) != 0) {
             j->rc = 3;
             break;
         }
         for (int b = 0; b < 65536; ++b) {
-            const uint16_t want = round_to_format(g_value[a] + g_value[b]);
+            const uint16_t want = reference(a, b);
             ++j->pairs;
             if (r0[b] != want || r1[b] != want) {
                 if (j->mismatches++ == 0) {
@@ -142,8 +160,8 @@ static void *worker(void *arg)
 
 int main(int argc, char **argv)
 {
-    if (argc != 5 && argc != 6) {
-        fprintf(stderr, "usage: %s ORACLE_SO DTYPE DECODE_TABLE THREADS [STEP]\n", argv[0]);
+    if (argc < 5 || argc > 7) {
+        fprintf(stderr, "usage: %s ORACLE_SO DTYPE DECODE_TABLE THREADS [STEP [OP]]\n", argv[0]);
         return 2;
     }
     void *lib = dlopen(argv[1], RTLD_NOW | RTLD_LOCAL);
@@ -175,8 +193,13 @@ int main(int argc, char **argv)
         return 2;
     }
     fclose(f);
-    if (argc == 6) g_step = atoi(argv[5]);
+    if (argc >= 6) g_step = atoi(argv[5]);
     if (g_step < 1) g_step = 1;
+    if (argc == 7) g_op = atoi(argv[6]);
+    if (g_op < 0 || g_op > 3) {
+        fprintf(stderr, "op must be 0 (SUM), 1 (MAX), 2 (MIN) or 3 (PROD)\n");
+        return 2;
+    }
     int nthreads = atoi(argv[4]);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 64) nthreads = 64;

@@ -1,5 +1,6 @@
 """Exhaustive pins of the oracle's 16-bit hop: every one of the 2^32 ordered
-pairs (a, b) of bfloat16 or binary16 bit patterns through its SUM fold.
+pairs (a, b) of bfloat16 or binary16 bit patterns through its SUM and PROD
+folds, and a strided sweep of the MAX and MIN selections.
 
 The per-hop fold of the post "Why AllReduce = ReduceScatter + AllGather -- with
 NCCL Ring AllReduce" (loosp.cn, section 5: the incoming partial is added to the
@@ -7,9 +8,12 @@ local one) is, for a 16-bit format, the exact sum rounded once to the format,
 nearest even.  The reference sits in tests/c/exhaustive_hop.c: both operands
 decoded by numpy (a table of all 65536 patterns), added in binary64 and rounded
 to the format by integer operations on the binary64 bits; a NaN result is the
-canonical quiet NaN.  It shares no code with the oracle, which it calls through
-dlopen.  About a minute on 8 cores (marked slow); a strided run checks that the
-same harness catches planted rounding mistakes.
+canonical quiet NaN.  PROD: the binary64 product of the two decoded values
+(exact) rounded the same way: the correctly rounded product.  MAX / MIN select the local operand if it compares greater (less)
+than the incoming one, else the incoming one.  The reference shares no code
+with the oracle, which it calls through dlopen.  About a minute per fold on 8
+cores (marked slow); strided runs check that the same harness catches planted
+mistakes.
 """
 import os
 import shutil
@@ -59,10 +63,11 @@ def _tables(bits):
     }
 
 
-def _run(harness, lib, dtype, step=1):
+def _run(harness, lib, dtype, step=1, op="sum"):
     exe, paths, _ = harness
     code = oracle.DTYPES[dtype]
-    run = subprocess.run([exe, lib, str(code), paths[dtype], str(_threads()), str(step)],
+    run = subprocess.run([exe, lib, str(code), paths[dtype], str(_threads()), str(step),
+                          str(oracle.OPS[op])],
                          capture_output=True, text=True, timeout=1200)
     assert run.returncode == 0, run.stdout + run.stderr
     first = run.stdout.split()
@@ -91,17 +96,40 @@ def test_every_pair_through_the_sum_fold(harness, dtype):
     assert mismatches == 0, out
 
 
-@pytest.mark.parametrize("dtype,old,new", [
-    ("bf16", "double n = nearbyint(ldexp(a, -q));", "double n = floor(ldexp(a, -q));"),
-    ("bf16", "if (q < -133) q = -133;", "if (q < -126) q = -126;"),
-    ("fp16", "double r = ldexp(nearbyint(ldexp(a, -q)), q);",
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_every_pair_through_the_prod_fold(harness, dtype):
+    """All 2^32 ordered operand pairs through the PROD fold."""
+    lib = oracle.build()
+    pairs, mismatches, out = _run(harness, lib, dtype, op="prod")
+    assert pairs == 1 << 32
+    assert mismatches == 0, out
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_max_min_selections(harness, dtype, op):
+    """Every 61st first operand against all 65536 second ones (70 million pairs,
+    every sign, zero, subnormal, infinity and NaN class on both sides)."""
+    lib = oracle.build()
+    pairs, mismatches, out = _run(harness, lib, dtype, step=61, op=op)
+    assert pairs == 1075 * 65536
+    assert mismatches == 0, out
+
+
+@pytest.mark.parametrize("dtype,op,old,new", [
+    ("bf16", "sum", "double n = nearbyint(ldexp(a, -q));", "double n = floor(ldexp(a, -q));"),
+    ("bf16", "sum", "if (q < -133) q = -133;", "if (q < -126) q = -126;"),
+    ("fp16", "sum", "double r = ldexp(nearbyint(ldexp(a, -q)), q);",
      "double r = ldexp(round(ldexp(a, -q)), q);"),
-    ("fp16", "if (r > 65504.0)", "if (r >= 65504.0)"),
+    ("fp16", "sum", "if (r > 65504.0)", "if (r >= 65504.0)"),
+    ("bf16", "prod", "lo[i] = bf16_from_double(a * b);", "lo[i] = bf16_from_double(a * a);"),
+    ("fp16", "max", "lo[i] = b > a ? lo[i] : in[i];", "lo[i] = b >= a ? lo[i] : in[i];"),
 ])
-def test_the_harness_catches_planted_rounding_mistakes(harness, dtype, old, new):
+def test_the_harness_catches_planted_mistakes(harness, dtype, op, old, new):
     """A strided run (every 257th first operand) against oracles with one
-    rounding mistake planted: each is caught, while the unmodified oracle
-    passes the same run."""
+    mistake planted in a fold or its rounding: each is caught, while the
+    unmodified oracle passes the same run."""
     _, _, d = harness
     with open(ORACLE_SRC) as f:
         text = f.read()
@@ -114,7 +142,7 @@ def test_the_harness_catches_planted_rounding_mistakes(harness, dtype, old, new)
         subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-w",
                         "-o", so, str(c), "-lm"], check=True)
         libs[tag] = so
-    pairs, mismatches, out = _run(harness, libs["ok"], dtype, step=257)
+    pairs, mismatches, out = _run(harness, libs["ok"], dtype, step=257, op=op)
     assert pairs == 256 * 65536 and mismatches == 0, out
-    _, mismatches, _ = _run(harness, libs["bad"], dtype, step=257)
+    _, mismatches, _ = _run(harness, libs["bad"], dtype, step=257, op=op)
     assert mismatches > 0
