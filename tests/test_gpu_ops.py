@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_util import assert_matches_oracle, log, oracle_expect, to_host, to_slabs, guards_intact
+from tests.gpu_util import (assert_full_matches, assert_matches_oracle, guards_intact, log,
+                            oracle_expect, to_host, to_slabs)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +145,27 @@ def test_specials_through_the_ring(rr, dtype, R):
         got = _run(rr, [t.copy() for t in x], dtype, op, 1)
         assert_matches_oracle(got, oracle_expect([t.copy() for t in x], op), dtype,
                               f"specials {dtype} R={R} {op}")
+
+
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_16bit_operand_pairs_through_the_hop(rr, dtype, op):
+    """Every 32nd 16-bit pattern as first operand against all 65536 as second
+    (134 million ordered pairs: every sign, zero, subnormal, infinity and NaN
+    class on both sides) through one fold of the ring on the GPU, bit for bit
+    against the oracle, whose folds are pinned on all 2^32 pairs on the CPU.
+    R = 2: rank 0 holds the first operands and rank 1 the second ones; each
+    position is folded once (rank 0's value into rank 1's in the first chunk,
+    the other way in the second) and both ranks end with the result."""
+    firsts = np.arange(0, 1 << 16, 32, dtype=np.uint16)
+    a = np.repeat(firsts, 1 << 16)
+    b = np.tile(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16), firsts.size)
+    x = [a, b] if dtype == "bf16" else [a.view(np.float16), b.view(np.float16)]
+    log(f"case 16-bit pairs {dtype} {op}: {a.size} pairs")
+    slabs = to_slabs(rr, x, dtype)
+    rr.allreduce_ring(slabs.ranks, op, 1)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(slabs, dtype, a.size), "a kernel wrote outside the rank buffers"
+    want = oracle_expect(x, op)
+    assert_full_matches(slabs.ranks, want, dtype, f"16-bit pairs {dtype} {op}")
