@@ -97,6 +97,10 @@ def parse():
                     help="instead of the headline: one call of the workload with a clock stamp "
                          "per (lane, rank, hop) (allreduce_ring_timed), summarised as wait "
                          "and move times per hop and the spread of hop ends across ranks")
+    ap.add_argument("--order-ab", action="store_true",
+                    help="instead of the headline: the in-place ring with the automatic hop "
+                         "order against every hop ascending, interleaved in one process, "
+                         "over R = 2..64 and 1 MiB..1 GiB per rank (one JSON line per point)")
     ap.add_argument("--barrier-latency", action="store_true",
                     help="instead of the AllReduce: per-step latency of the counting barrier "
                          "alone for R = 2..64 and 1 or 8 contexts (one JSON line per point)")
@@ -381,6 +385,8 @@ def main():
         return host_cost(rr, torch)
     if args.r16_sweep:
         return r16_sweep(rr, torch, np, args.layout)
+    if args.order_ab:
+        return order_ab(rr, torch)
     w = pick_workload(args.workload)
     if args.sync:
         w = w.with_(sync=args.sync)
@@ -718,6 +724,69 @@ def r16_sweep(rr, torch, np, layout="separate"):
                                   "stream_loads": p["stream_loads"], "alternate": p["alternate"],
                                   "launches": p["launches"]}),
                       flush=True)
+        del ranks, restore
+        torch.cuda.empty_cache()
+    return 0
+
+
+def order_ab(rr, torch):
+    """The automatic hop order (even hops top down once the R buffers exceed
+    128 MiB) against every hop ascending (RR_FLAG_ASCENDING), in one process on
+    one set of buffers: fp32 SUM over R = 2..64 and 1 MiB..1 GiB per rank (up to
+    16 GiB in all), bf16 at three points, both hand-off modes.  Per point and
+    order: three repetitions, interleaved, of 2 warm-up and 5 timed calls, each
+    after the inputs are restored outside its events; the median of the three
+    medians is reported.  Uniform inputs in [-1, 1) from torch's generator."""
+    rr.init()
+    stream = torch.cuda.current_stream()
+    cases = []
+    for R in (2, 4, 8, 16, 32, 64):
+        for mib in (1, 16, 64, 256, 1024):
+            if R * mib > 16384 or (R >= 32 and mib > 256):
+                continue
+            for sync in ("p2p", "barrier"):
+                cases.append((R, mib, "fp32", sync))
+    for R, mib in ((8, 256), (16, 256), (64, 32)):
+        for sync in ("p2p", "barrier"):
+            cases.append((R, mib, "bf16", sync))
+    for R, mib, dt, sync in cases:
+        tdt = torch.float32 if dt == "fp32" else torch.bfloat16
+        count = mib * (1 << 20) // (4 if dt == "fp32" else 2)
+        ns = 16 if R == 16 else 8
+        g = torch.Generator(device="cuda")
+        g.manual_seed(R * 131 + mib)
+        ranks, snapshot = rank_buffers(rr, torch, R, count, tdt, "separate")
+        for t in ranks:
+            t.uniform_(-1, 1, generator=g)
+        restore = snapshot()
+        p = rr.plan(R, count, dt, ns, sync=sync)
+        orders = {"auto": dict(sync=sync), "ascending": dict(sync=sync, order="ascending")}
+        med = {k: [] for k in orders}
+        for _ in range(3):
+            for k, o in orders.items():
+                for _ in range(2):
+                    restore()
+                    rr.allreduce_ring(ranks, "sum", ns, **o)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(5)]
+                for a, e in evs:
+                    restore()
+                    a.record(stream)
+                    rr.allreduce_ring(ranks, "sum", ns, **o)
+                    e.record(stream)
+                torch.cuda.synchronize()
+                rr.check_kernel_error()
+                med[k].append(sorted(a.elapsed_time(e) for a, e in evs)[2])
+        ms = {k: sorted(v)[1] for k, v in med.items()}
+        B = p["hbm_bytes"]
+        print(json.dumps({"metric": "hop order A/B", "R": R, "bytes_per_rank": mib << 20,
+                          "dtype": dt, "sync": p["sync"], "alternate": p["alternate"],
+                          "team": p["team"], "depth": p["depth"], "rounds": p["rounds"],
+                          "block": p["block"], "auto_ms": round(ms["auto"], 5),
+                          "ascending_ms": round(ms["ascending"], 5),
+                          "auto_pct": round(100 * B / ms["auto"] / 1e6 / HBM_PEAK_GBS, 2),
+                          "ascending_pct": round(100 * B / ms["ascending"] / 1e6 / HBM_PEAK_GBS, 2),
+                          "speedup": round(ms["ascending"] / ms["auto"], 4)}), flush=True)
         del ranks, restore
         torch.cuda.empty_cache()
     return 0
