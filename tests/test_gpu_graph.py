@@ -69,6 +69,8 @@ def _replay_and_check(rr, g, restore, read, expect, dtype, what):
     (4, 1000, "int32", "max", 1, "launch", 0),           # one launch per hop: 6 kernels
     (8, 1 << 16, "fp32", "sum", 4, "p2p", "fused"),
     (64, 8 * 1024 + 4, "fp32", "sum", 8, "barrier", 0),
+    (16, 65536 + 3, "fp32", "sum", 4, "barrier", "alternate"),  # the alternating kernel
+    (4, 1000, "bf16", "sum", 1, "launch", "alternate"),          # ... one launch per hop
 ])
 def test_ring_allreduce_replays(rr, R, count, dtype, op, ns, sync, flags):
     log(f"case graph ring R={R} count={count} {dtype} {op} ns={ns} sync={sync} flags={flags}")
@@ -77,7 +79,11 @@ def test_ring_allreduce_replays(rr, R, count, dtype, op, ns, sync, flags):
     expect = oracle_expect(x, op)
     slabs = to_slabs(rr, x, dtype)
     pristine = slabs.storage.clone()
-    opts = dict(sync=sync, fused=True) if flags == "fused" else dict(sync=sync)
+    opts = dict(sync=sync)
+    if flags == "fused":
+        opts["fused"] = True
+    elif flags == "alternate":
+        opts["order"] = "alternate"
 
     def call():
         rr.allreduce_ring(slabs.ranks, op, ns, **opts)
