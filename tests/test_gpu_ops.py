@@ -169,3 +169,25 @@ def test_16bit_operand_pairs_through_the_hop(rr, dtype, op):
     assert guards_intact(slabs, dtype, a.size), "a kernel wrote outside the rank buffers"
     want = oracle_expect(x, op)
     assert_full_matches(slabs.ranks, want, dtype, f"16-bit pairs {dtype} {op}")
+
+
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min"])
+@pytest.mark.parametrize("dtype", ["fp32", "int32"])
+def test_32bit_random_patterns_through_the_hop(rr, dtype, op):
+    """64 million ordered pairs of uniformly random 32-bit patterns (for fp32:
+    every class -- normal, subnormal, zero, infinity, NaN with any payload --
+    in proportion to its share of the patterns) through one fold of the ring on
+    the GPU, against the oracle (fp32 NaNs compare as NaN whatever the payload).
+    R = 2, as in the 16-bit test above."""
+    rng = np.random.default_rng(4242 + len(op))
+    a = rng.integers(0, 1 << 32, size=1 << 26, dtype=np.uint64).astype(np.uint32)
+    b = rng.integers(0, 1 << 32, size=1 << 26, dtype=np.uint64).astype(np.uint32)
+    view = np.float32 if dtype == "fp32" else np.int32
+    x = [a.view(view), b.view(view)]
+    log(f"case 32-bit patterns {dtype} {op}: {a.size} pairs")
+    slabs = to_slabs(rr, x, dtype)
+    rr.allreduce_ring(slabs.ranks, op, 1)
+    torch.cuda.synchronize()
+    rr.check_kernel_error()
+    assert guards_intact(slabs, dtype, a.size), "a kernel wrote outside the rank buffers"
+    assert_full_matches(slabs.ranks, oracle_expect(x, op), dtype, f"32-bit patterns {dtype} {op}")
